@@ -1,0 +1,251 @@
+// api.hip -- the C ABI declared in include/dsa.h: argument validation (all of
+// it on the host, before any HIP call), the once-per-device architecture
+// check, and dispatch to the launchers.
+//
+// Rejections follow the SGLang pages: a latent width other than the rows'
+// 512 and E4M3FNUZ are refused before any kernel is dispatched ("extend CUDA
+// TileLang raw FP8 KV path", Modifications); the geometry is passed as
+// required integers and checked, not inferred from a model name, and a
+// nonzero RoPE width (the 656-byte layout) is refused ("[DSA] Support
+// flashmla_sparse_q8 prefill backend on CUDA", review thread).
+#include <atomic>
+#include <cstring>
+
+#include "../../include/dsa.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+int32_t check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return DSA_ERR_DEVICE;
+    int st = g_arch_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DSA_ERR_DEVICE;
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_state[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? DSA_OK : DSA_ERR_DEVICE;
+}
+
+int32_t check_fp8_format(int32_t f) {
+    return f == DSA_FP8_E4M3FN ? DSA_OK : DSA_ERR_DTYPE;
+}
+
+int32_t check_layout(int32_t layout) {
+    return (layout == DSA_KV_RAW_FP8_512 || layout == DSA_KV_SCALED_FP8_528)
+               ? DSA_OK
+               : DSA_ERR_LAYOUT;
+}
+
+// Shared validation of the two attention entry points.
+int32_t validate_attn(const void *q, int32_t q_dtype, const float *q_scale,
+                      int32_t T, int32_t H, int32_t D, int32_t rope_dim,
+                      const void *pool, int64_t num_slots, int32_t layout,
+                      int32_t fp8_format, const int32_t *topk, int32_t K,
+                      const int32_t *page_table, int32_t page_size,
+                      int32_t max_pages, int32_t num_seqs,
+                      const int32_t *token_seq, const int32_t *seq_lens,
+                      void *out, int32_t out_dtype, void *workspace,
+                      size_t workspace_bytes, int32_t phase) {
+    if (D != 512) return DSA_ERR_WIDTH_MISMATCH;
+    if (rope_dim != 0) return DSA_ERR_LAYOUT;
+    int32_t st = check_layout(layout);
+    if (st) return st;
+    if ((st = check_fp8_format(fp8_format))) return st;
+    if (q_dtype != DSA_BF16 && q_dtype != DSA_FP8_E4M3FN) return DSA_ERR_DTYPE;
+    if (out_dtype != DSA_BF16 && out_dtype != DSA_FP32) return DSA_ERR_DTYPE;
+    if (T < 0 || H < 1 || H > 128) return DSA_ERR_SHAPE;
+    if (K <= 0 || K % 128 != 0 || K > 65536) return DSA_ERR_SHAPE;
+    if (num_slots < 0) return DSA_ERR_SHAPE;
+    if (page_table) {
+        if (page_size < 1 || (page_size & (page_size - 1)) != 0 || page_size > (1 << 20))
+            return DSA_ERR_SHAPE;
+        if (max_pages < 1) return DSA_ERR_SHAPE;
+    }
+    if ((page_table || seq_lens) && num_seqs < 1) return DSA_ERR_SHAPE;
+    if ((page_table || seq_lens) && !token_seq && T > num_seqs) return DSA_ERR_SHAPE;
+    if (T == 0) return DSA_OK;
+    if (!q || !pool || !topk || !out) return DSA_ERR_NULL;
+    if (q_dtype == DSA_FP8_E4M3FN && !q_scale) return DSA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(pool) || !aligned16(out)) return DSA_ERR_ALIGN;
+    const size_t need = dsa::attn_workspace_bytes(T, H, K, phase);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
+        if (!aligned256(workspace)) return DSA_ERR_ALIGN;
+    }
+    return DSA_OK;
+}
+
+int32_t run_attn(int32_t phase, const void *q, int32_t q_dtype,
+                 const float *q_scale, int32_t T, int32_t H, int32_t D,
+                 int32_t rope_dim, const void *pool, int64_t num_slots,
+                 int32_t layout, int32_t fp8_format, const int32_t *topk,
+                 int32_t K, const int32_t *page_table, int32_t page_size,
+                 int32_t max_pages, int32_t num_seqs, const int32_t *token_seq,
+                 const int32_t *seq_lens, float softmax_scale, void *out,
+                 int32_t out_dtype, float *lse, void *workspace,
+                 size_t workspace_bytes, int32_t *err_count, void *stream) {
+    int32_t st = validate_attn(q, q_dtype, q_scale, T, H, D, rope_dim, pool,
+                               num_slots, layout, fp8_format, topk, K,
+                               page_table, page_size, max_pages, num_seqs,
+                               token_seq, seq_lens, out, out_dtype, workspace,
+                               workspace_bytes, phase);
+    if (st != DSA_OK || T == 0) return st;
+    if ((st = check_device())) return st;
+
+    dsa::AttnArgs a;
+    a.q = q;
+    a.q_scale = q_scale;
+    a.T = T;
+    a.H = H;
+    a.pool = static_cast<const uint8_t *>(pool);
+    a.num_slots = num_slots;
+    a.topk = topk;
+    a.K = K;
+    a.page_table = page_table;
+    int shift = 0;
+    if (page_table)
+        while ((1 << shift) < page_size) shift++;
+    a.page_shift = shift;
+    a.max_pages = max_pages;
+    a.num_seqs = num_seqs;
+    a.token_seq = token_seq;
+    a.seq_lens = seq_lens;
+    a.softmax_scale = softmax_scale;
+    a.out = out;
+    a.lse = lse;
+    a.ws = static_cast<float *>(workspace);
+    a.n_splits = phase == 0 ? dsa::attn_decode_splits(T, H, K) : 1;
+    a.split_len = 0;
+    a.err_count = err_count;
+    hipError_t e = dsa::launch_attn(a, layout, q_dtype == DSA_FP8_E4M3FN,
+                                    out_dtype == DSA_BF16,
+                                    static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_kv_row_bytes(int32_t layout) {
+    if (layout == DSA_KV_RAW_FP8_512) return 512;
+    if (layout == DSA_KV_SCALED_FP8_528) return 528;
+    return -1;
+}
+
+const char *dsa_status_string(int32_t status) {
+    switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_NULL: return "DSA_ERR_NULL";
+    case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE";
+    case DSA_ERR_WIDTH_MISMATCH: return "DSA_ERR_WIDTH_MISMATCH";
+    case DSA_ERR_LAYOUT: return "DSA_ERR_LAYOUT";
+    case DSA_ERR_DTYPE: return "DSA_ERR_DTYPE";
+    case DSA_ERR_ALIGN: return "DSA_ERR_ALIGN";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_DEVICE: return "DSA_ERR_DEVICE";
+    case DSA_ERR_LAUNCH: return "DSA_ERR_LAUNCH";
+    default: return "DSA_ERR_UNKNOWN";
+    }
+}
+
+int32_t dsa_kv_write(const void *kv, int64_t n, int64_t kv_row_stride,
+                     int32_t kv_dtype, int32_t kv_dim, int32_t rope_dim,
+                     const int64_t *slot_mapping, void *pool,
+                     int64_t num_slots, int32_t layout, int32_t fp8_format,
+                     int32_t *err_count, void *stream) {
+    if (kv_dim != 512) return DSA_ERR_WIDTH_MISMATCH;
+    if (rope_dim != 0) return DSA_ERR_LAYOUT;
+    int32_t st = check_layout(layout);
+    if (st) return st;
+    if ((st = check_fp8_format(fp8_format))) return st;
+    if (kv_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (n < 0 || num_slots < 0 || kv_row_stride < 512) return DSA_ERR_SHAPE;
+    if (n > ((int64_t)1 << 33)) return DSA_ERR_SHAPE;
+    if (n == 0) return DSA_OK;
+    if (!kv || !slot_mapping || !pool) return DSA_ERR_NULL;
+    if (!aligned16(kv) || !aligned16(pool) || (kv_row_stride * 2) % 16 != 0)
+        return DSA_ERR_ALIGN;
+    if ((st = check_device())) return st;
+    hipError_t e = dsa::launch_kv_write(
+        static_cast<const uint16_t *>(kv), n, kv_row_stride, slot_mapping,
+        static_cast<uint8_t *>(pool), num_slots, layout, err_count,
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
+size_t dsa_quantize_q_workspace_bytes(int64_t n_elems) {
+    if (n_elems <= 0) return 0;
+    return (size_t)dsa::quantize_q_blocks(n_elems) * sizeof(float);
+}
+
+int32_t dsa_quantize_q_fp8(const void *q, int64_t n_elems, int32_t q_dtype,
+                           void *q8, float *q_scale, int32_t scale_given,
+                           int32_t fp8_format, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    int32_t st = check_fp8_format(fp8_format);
+    if (st) return st;
+    if (q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (n_elems < 0 || n_elems % 8 != 0) return DSA_ERR_SHAPE;
+    if (n_elems == 0) return DSA_OK;
+    if (!q || !q8 || !q_scale) return DSA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(q8)) return DSA_ERR_ALIGN;
+    if (!scale_given) {
+        if (!workspace || workspace_bytes < dsa_quantize_q_workspace_bytes(n_elems))
+            return DSA_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return DSA_ERR_ALIGN;
+    }
+    if ((st = check_device())) return st;
+    hipError_t e = dsa::launch_quantize_q(
+        static_cast<const uint16_t *>(q), n_elems, static_cast<uint8_t *>(q8),
+        q_scale, scale_given != 0, static_cast<float *>(workspace),
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
+size_t dsa_attn_workspace_bytes(int32_t T, int32_t H, int32_t K, int32_t phase) {
+    if (T <= 0 || H <= 0 || K <= 0 || K % 128 != 0) return 0;
+    return dsa::attn_workspace_bytes(T, H, K, phase);
+}
+
+int32_t dsa_sparse_attn_decode(
+    const void *q, int32_t q_dtype, const float *q_scale, int32_t T, int32_t H,
+    int32_t D, int32_t rope_dim, const void *pool, int64_t num_slots,
+    int32_t layout, int32_t fp8_format, const int32_t *topk, int32_t K,
+    const int32_t *page_table, int32_t page_size, int32_t max_pages,
+    int32_t num_seqs, const int32_t *token_seq, const int32_t *seq_lens,
+    float softmax_scale, void *out, int32_t out_dtype, float *lse,
+    void *workspace, size_t workspace_bytes, int32_t *err_count, void *stream) {
+    return run_attn(0, q, q_dtype, q_scale, T, H, D, rope_dim, pool, num_slots,
+                    layout, fp8_format, topk, K, page_table, page_size,
+                    max_pages, num_seqs, token_seq, seq_lens, softmax_scale,
+                    out, out_dtype, lse, workspace, workspace_bytes, err_count,
+                    stream);
+}
+
+int32_t dsa_sparse_attn_prefill(
+    const void *q, int32_t q_dtype, const float *q_scale, int32_t T, int32_t H,
+    int32_t D, int32_t rope_dim, const void *pool, int64_t num_slots,
+    int32_t layout, int32_t fp8_format, const int32_t *topk, int32_t K,
+    const int32_t *page_table, int32_t page_size, int32_t max_pages,
+    int32_t num_seqs, const int32_t *token_seq, const int32_t *seq_lens,
+    float softmax_scale, void *out, int32_t out_dtype, float *lse,
+    void *workspace, size_t workspace_bytes, int32_t *err_count, void *stream) {
+    return run_attn(1, q, q_dtype, q_scale, T, H, D, rope_dim, pool, num_slots,
+                    layout, fp8_format, topk, K, page_table, page_size,
+                    max_pages, num_seqs, token_seq, seq_lens, softmax_scale,
+                    out, out_dtype, lse, workspace, workspace_bytes, err_count,
+                    stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// common.h -- device-side types and helpers shared by the gfx950 kernels.
+//
+// FP8 here is the OCP E4M3FN format (bias 7, no infinities, S.1111.111 is
+// NaN), the flavour the SGLang pages require on this path ("extend CUDA
+// TileLang raw FP8 KV path", Modifications: E4M3FNUZ is rejected).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 512;          // latent width (kv_lora_rank)
+constexpr int kGroup = 128;      // elements per scale group (528-byte rows)
+constexpr int kRawBytes = 512;
+constexpr int kScaledBytes = 528;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
+    return __uint_as_float(h16 << 16);
+}
+
+// fp32 -> E4M3FN code: round to nearest even, +-inf and finite values whose
+// magnitude is at least 448 saturate to +-448 (0x7E), NaN -> 0x7F with the
+// input's sign, -0 -> 0x80.  Written on the fp32 bit pattern:
+//   |x| <  2^-6  : subnormal band, code = rint(|x| * 2^9)  (0..8; 8 is the
+//                  smallest normal's code 0x08);
+//   2^-6 <= |x| < 448 : add half an ulp of a 3-bit mantissa (ties to even) at
+//                  bit 20 and re-bias the exponent from 127 to 7.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+    uint32_t u = __float_as_uint(x);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return sign | 0x7fu;          // NaN
+    if (a >= 0x43e00000u) return sign | 0x7eu;         // >= 448 (and inf)
+    if (a < 0x3c800000u) {                             // < 2^-6
+        float t = __uint_as_float(a) * 512.0f;         // exact scaling
+        return sign | (uint32_t)__builtin_rintf(t);
+    }
+    uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+    uint32_t e = (r >> 23) - 120u;                     // 127 -> 7
+    uint32_t m = (r >> 20) & 7u;
+    return sign | (e << 3) | m;
+}
+
+// Four fp32 -> four E4M3FN codes packed little-endian in a uint32.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+    return f32_to_e4m3(a) | (f32_to_e4m3(b) << 8) | (f32_to_e4m3(c) << 16) |
+           (f32_to_e4m3(d) << 24);
+}
+
+// Exact E4M3FN -> bf16 / f16 conversions of the two codes in the low (hi =
+// false) or high half of a 32-bit word, through gfx950's OCP FP8 converts
+// with a unit scale.
+template <bool HI>
+__device__ __forceinline__ bf16x2 e4m3x2_to_bf16(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI);
+}
+template <bool HI>
+__device__ __forceinline__ f16x2 e4m3x2_to_f16(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HI);
+}
+
+// Eight codes (two little-endian words) -> bf16x8 / f16x8, element order kept.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+    bf16x2 a = e4m3x2_to_bf16<false>(w0), b = e4m3x2_to_bf16<true>(w0);
+    bf16x2 c = e4m3x2_to_bf16<false>(w1), d = e4m3x2_to_bf16<true>(w1);
+    bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return r;
+}
+__device__ __forceinline__ f16x8 e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
+    f16x2 a = e4m3x2_to_f16<false>(w0), b = e4m3x2_to_f16<true>(w0);
+    f16x2 c = e4m3x2_to_f16<false>(w1), d = e4m3x2_to_f16<true>(w1);
+    f16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return r;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+}  // namespace dsa

@@ -195,7 +195,7 @@ def scaled_decode(seed: int = 3) -> Workload:
 
 
 def q8_prefill(seed: int = 4, prefix: int = 16384, T: int = 4096,
-               H: int = 32, K: int = 2048) -> Workload:
+               H: int = 32, K: int = 2048, num_slots: int = 1 << 20) -> Workload:
     """``T`` new query tokens appended to a ``prefix``-token sequence.  The
     writer first casts the new bf16 latents to raw FP8 and scatters them into
     their slots; the query is cast to FP8 with one per-tensor scale.  Token i
@@ -204,7 +204,7 @@ def q8_prefill(seed: int = 4, prefix: int = 16384, T: int = 4096,
     K-128 distinct uniform positions of [0, p-128], shuffled.  Where fewer
     than K positions exist, the valid ones come first and -1 pads the row."""
     r_pool, r_pages, r_q, r_topk, r_x = _streams(seed)
-    page_size, num_slots = 64, 1 << 20
+    page_size = 64
     L = prefix + T
     pt = _place_pages(r_pages, [-(-L // page_size)], num_slots // page_size)
     topk = np.full((T, K), -1, np.int32)
