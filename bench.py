@@ -1,0 +1,269 @@
+"""Throughput of the DSA sparse-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one pass of the hot path over one batch: the fused writer appends
+each sequence's newest latent to the paged FP8 pool, then sparse attention
+runs over every token's top-k rows (decode: split top-k + merge kernel;
+the Q8 prefill workload also casts the query to FP8 first).  Inputs are
+resident in HBM before the timed region.  Consecutive steps rotate over
+several independent layer pools (as consecutive layers of a model do) so
+that at least 1 GiB of rows is gathered per rotation and the 256 MB
+Infinity Cache cannot serve the step from the previous visit.
+
+Prints ONE JSON line.  `value` is query tokens per second of the whole step
+loop; `roofline` relates the attention call's algorithmic bytes (decode:
+gathered row bytes) or FLOPs (prefill) to its duration measured with HIP
+events on the launch stream; `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_TFLOPS = 2500.0       # dense bf16/f16 matrix peak, published
+METRIC = "query tok/s + gathered-KV GB/s (% HBM peak), decode H=16 top-k=2048"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_batch",
+                    choices=["decode_batch", "scaled_decode", "mixed_decode",
+                             "q8_prefill", "tiny_decode"])
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layer pools to rotate over (0 = enough for 1 GiB)")
+    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "fp32"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter scaling)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus N with N > 1 "
+              "is not supported (no sharding or collectives on this path)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_mla_attention_gather_amd as dsa
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    wl = W.NAMED[args.workload]()
+    T, H, K, R = wl.T, wl.H, wl.K, wl.row_bytes
+    prefill = wl.q_fp8
+    phase = 1 if prefill else 0
+    out_dtype = dsa.DSA_BF16 if args.out_dtype == "bf16" else dsa.DSA_FP32
+
+    valid_entries = int(np.sum(wl.topk >= 0))
+    gathered = valid_entries * R                       # algorithmic bytes / call
+    flops = 4.0 * H * 512 * valid_entries              # QK + PV per call
+    if args.layers > 0:
+        layers = args.layers
+    else:
+        layers = max(2, min(16, math.ceil((1 << 30) / max(gathered, 1))))
+        if prefill:
+            layers = 2
+    print(f"bench: {wl.name} T={T} H={H} K={K} rows={R}B valid={valid_entries} "
+          f"layers={layers}", file=sys.stderr, flush=True)
+
+    # ---- device inputs (shared index tensors, per-layer pools and queries)
+    topk = torch.from_numpy(wl.topk).to(dev)
+    pt = torch.from_numpy(wl.page_table).to(dev)
+    sl = torch.from_numpy(wl.seq_lens).to(dev)
+    ts = None if wl.token_seq is None else torch.from_numpy(wl.token_seq).to(dev)
+    num_seqs, max_pages = wl.page_table.shape
+    kv_new = torch.from_numpy(wl.kv_new.view(np.int16)).to(dev)
+    slot_map = torch.from_numpy(wl.slot_mapping).to(dev)
+    n_new = wl.kv_new.shape[0]
+    used = torch.from_numpy(wl.page_slots(wl.used_pages())).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    pools, qs = [], []
+    for layer in range(layers):
+        pool = torch.full((wl.num_slots, R), 0xFF, dtype=torch.uint8, device=dev)
+        # fill every used page through the writer from N(0,1) latents
+        chunk = 1 << 18
+        for i in range(0, used.numel(), chunk):
+            sl_i = used[i:i + chunk]
+            lat = torch.randn((sl_i.numel(), 512), generator=gen, device=dev,
+                              dtype=torch.float32).to(torch.bfloat16)
+            dsa.check(dsa.dsa_kv_write(lat, sl_i.numel(), 512, dsa.DSA_BF16, 512, 0,
+                                       sl_i, pool, wl.num_slots, wl.layout,
+                                       dsa.DSA_FP8_E4M3FN))
+        pools.append(pool)
+        qs.append(torch.randn((T, H, 512), generator=gen, device=dev,
+                              dtype=torch.float32).to(torch.bfloat16))
+    torch.cuda.synchronize()
+
+    out = torch.empty((T, H, 512), device=dev,
+                      dtype=torch.bfloat16 if out_dtype == dsa.DSA_BF16 else torch.float32)
+    lse = torch.empty((T, H), device=dev, dtype=torch.float32)
+    wsb = dsa.dsa_attn_workspace_bytes(T, H, K, phase)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    q8 = torch.empty((T, H, 512), dtype=torch.uint8, device=dev)
+    q_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    qwsb = dsa.dsa_quantize_q_workspace_bytes(T * H * 512)
+    qws = torch.empty(max(qwsb, 4), dtype=torch.uint8, device=dev)
+    attn = dsa.dsa_sparse_attn_prefill if prefill else dsa.dsa_sparse_attn_decode
+
+    def step(i, ev=None):
+        layer = i % layers
+        pool = pools[layer]
+        dsa.check(dsa.dsa_kv_write(kv_new, n_new, 512, dsa.DSA_BF16, 512, 0,
+                                   slot_map, pool, wl.num_slots, wl.layout,
+                                   dsa.DSA_FP8_E4M3FN))
+        if prefill:
+            dsa.check(dsa.dsa_quantize_q_fp8(qs[layer], T * H * 512, dsa.DSA_BF16,
+                                             q8, q_scale, 0, dsa.DSA_FP8_E4M3FN,
+                                             qws, qwsb))
+            q, qd, qsc = q8, dsa.DSA_FP8_E4M3FN, q_scale
+        else:
+            q, qd, qsc = qs[layer], dsa.DSA_BF16, None
+        if ev is not None:
+            ev[0].record()
+        dsa.check(attn(q, qd, qsc, T, H, 512, 0, pool, wl.num_slots, wl.layout,
+                       dsa.DSA_FP8_E4M3FN, topk, K, pt, wl.page_size, max_pages,
+                       num_seqs, ts, sl, wl.softmax_scale, out, out_dtype, lse,
+                       ws, wsb, None))
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in events]
+    attn_avg_s = float(np.mean(attn_ms)) * 1e-3
+    tok_s = T * args.steps / elapsed
+
+    if prefill:
+        achieved = flops / attn_avg_s / 1e12
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_TFLOPS,
+                    "traffic": None}
+    else:
+        achieved = gathered / attn_avg_s / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None}
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "T": T, "H": H, "top_k": K,
+            "valid_entries": valid_entries, "kv_row_bytes": R,
+            "pool_slots": wl.num_slots, "page_size": wl.page_size,
+            "q": "fp8_e4m3fn per-tensor scale" if prefill else "bf16",
+            "out": args.out_dtype, "layer_pools": layers,
+        },
+        "attn_us": attn_avg_s * 1e6,
+        "attn_us_p10_p90": [float(np.percentile(attn_ms, 10)) * 1e3,
+                            float(np.percentile(attn_ms, 90)) * 1e3],
+        "gathered_GBps": gathered / attn_avg_s / 1e9,
+        "gathered_bytes_per_call": gathered,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle (as it stands) on a bounded sample of the same workload:
+    whole steps (writer on the new rows + attention for every token of the
+    batch) over a host pool whose used pages hold random finite FP8 codes,
+    repeated until about `budget_s` seconds have passed."""
+    import oracle
+    import workloads as W
+
+    orc = oracle.get()
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    R = wl.row_bytes
+    rng = np.random.default_rng(wl.seed + 1000)
+    T_s = wl.T
+    if wl.q_fp8:
+        T_s = min(wl.T, 64)     # prefill: a token slice of the batch
+    pool = np.zeros((wl.num_slots, R), np.uint8)
+    slots = wl.page_slots(wl.used_pages())
+    pool[slots, :512] = W.random_fp8_codes(rng, (len(slots), 512))
+    if R == 528:
+        pool[slots, 512:] = W.log_uniform_scales(rng, len(slots)).view(np.uint8)
+    sel = slice(0, T_s)
+    q = wl.q[sel]
+    q8 = scale = None
+    steps, tokens, t_total = 0, 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        orc.kv_write(wl.kv_new, wl.slot_mapping, pool, wl.layout)
+        if wl.q_fp8:
+            scale = orc.q_scale(q)
+            q8 = orc.q_quantize(q, scale)
+        orc.sparse_attn(q if q8 is None else q8, pool, wl.layout, wl.topk[sel],
+                        wl.softmax_scale, q_scale=scale, page_table=wl.page_table,
+                        page_size=wl.page_size,
+                        token_seq=None if wl.token_seq is None else wl.token_seq[sel],
+                        seq_lens=wl.seq_lens, nthreads=cores)
+        t_total += time.perf_counter() - t0
+        steps += 1
+        tokens += T_s
+        if t_total >= budget_s or steps >= 50:
+            break
+    return {"value": tokens / t_total, "unit": "tok/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{steps} step(s) of {wl.name}: writer on the {wl.kv_new.shape[0]} "
+                      f"new rows + FP64 attention for {T_s} tokens x {wl.H} heads x "
+                      f"top-k {wl.K}; {t_total:.1f} s on {cores} threads"}
+
+
+if __name__ == "__main__":
+    main()

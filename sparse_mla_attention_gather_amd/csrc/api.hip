@@ -65,7 +65,7 @@ int32_t validate_attn(const void *q, int32_t q_dtype, const float *q_scale,
     if (out_dtype != DSA_BF16 && out_dtype != DSA_FP32) return DSA_ERR_DTYPE;
     if (T < 0 || H < 1 || H > 128) return DSA_ERR_SHAPE;
     if (K <= 0 || K % 128 != 0 || K > 65536) return DSA_ERR_SHAPE;
-    if (num_slots < 0) return DSA_ERR_SHAPE;
+    if (num_slots < 0 || num_slots >= ((int64_t)1 << 31)) return DSA_ERR_SHAPE;
     if (page_table) {
         if (page_size < 1 || (page_size & (page_size - 1)) != 0 || page_size > (1 << 20))
             return DSA_ERR_SHAPE;
@@ -124,7 +124,7 @@ int32_t run_attn(int32_t phase, const void *q, int32_t q_dtype,
     a.out = out;
     a.lse = lse;
     a.ws = static_cast<float *>(workspace);
-    a.n_splits = phase == 0 ? dsa::attn_decode_splits(T, H, K) : 1;
+    a.n_splits = dsa::attn_splits(T, H, K, phase);
     a.split_len = 0;
     a.err_count = err_count;
     hipError_t e = dsa::launch_attn(a, layout, q_dtype == DSA_FP8_E4M3FN,

@@ -40,8 +40,9 @@ struct AttnArgs {
     int32_t *err_count;
 };
 
-// Number of top-k splits the decode path uses for this shape (1 = none).
+// Number of top-k splits for this shape and phase (1 = none).
 int attn_decode_splits(int T, int H, int K);
+int attn_splits(int T, int H, int K, int phase);
 size_t attn_workspace_bytes(int T, int H, int K, int phase);
 
 hipError_t launch_attn(const AttnArgs &a, int layout, bool q_fp8, bool out_bf16,

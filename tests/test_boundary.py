@@ -119,6 +119,7 @@ REJECT = [
     (dict(H=129), "DSA_ERR_SHAPE"),
     (dict(T=-1), "DSA_ERR_SHAPE"),
     (dict(num_slots=-5), "DSA_ERR_SHAPE"),
+    (dict(num_slots=1 << 31), "DSA_ERR_SHAPE"),    # slots are held as int32
     (dict(page_size=48), "DSA_ERR_SHAPE"),
     (dict(page_size=0), "DSA_ERR_SHAPE"),
     (dict(max_pages=0), "DSA_ERR_SHAPE"),
