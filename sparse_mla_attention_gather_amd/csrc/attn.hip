@@ -8,44 +8,46 @@
 // multiset of valid entries; all-masked tokens give 0 (lse = -inf).
 //
 // Work decomposition: one workgroup (8 wavefronts) owns one unit = (token t,
-// block of 16 heads) and one split of t's top-k list (at most 2048 entries).
-// All 16 heads share every gathered row, so Q.X^T is a real
-// [16 x 512] x [512 x entries] contraction for the matrix cores.
+// block of 16 NT heads, NT = 1 or 2) and one split of t's top-k list (at most
+// 2048 entries).  All heads of the block share every gathered row, so Q.X^T
+// is a real [16NT x 512] x [512 x entries] contraction for the matrix cores,
+// and a row is gathered once per block of up to 32 heads.
 //
 //   prologue: the split's indices are resolved once (top-k value -> page
 //     table -> slot; -1 for padding and for invalid values, which are also
-//     counted) into LDS;
+//     counted) into LDS, every phase's loads issued before one wait;
 //   gather:   rows move HBM -> LDS with global_load_lds_dwordx4 (16 bytes per
 //     lane, no registers), 64-row tiles in 4 LDS buffers, 3 tiles in flight
 //     while one is computed, every wave issuing a share of each tile; the
 //     16-byte chunks of row r are stored XOR-swizzled by (r & 7) so that the
 //     matrix-operand reads below spread over the LDS banks; masked entries
-//     read a static zero row;
+//     read zero rows;
 //   QK^T:     wave w forms the partial S^T of entries 16(w%4) .. +16 over the
-//     dims half w/4 with v_mfma_f32_16x16x32_bf16 (rows FP8 -> bf16 exactly;
-//     an FP8 query is converted exactly too and its scale folded into the
-//     score scale); the two halves are summed through LDS;
+//     dims half w/4; bf16 query: v_mfma_f32_16x16x32_bf16 on rows converted
+//     FP8 -> bf16 exactly; FP8 query: v_mfma_scale_f32_16x16x128_f8f6f4 on
+//     the codes themselves (unit block scales), the query scale folded into
+//     the score scale.  The two halves are summed through LDS;
 //   softmax:  the waves agree on the tile max per head through LDS (online
 //     softmax, log2e folded into the scale) and publish P;
 //   PV:       wave w accumulates O^T for dims [64w, 64w+64) over the 64
 //     entries with v_mfma_f32_16x16x32_f16; its A operand (8 entries x 1 dim
 //     per lane) comes straight from the row-major tile through the gfx950
-//     LDS transpose read ds_read_b64_tr_b8; P is rounded to f16.  528-byte
-//     rows: group scales multiply the QK partial sums per 128-wide group
-//     and, in PV, multiply P (normalised per tile by the largest scale, the
-//     factor applied to the tile's f32 product);
+//     LDS transpose read ds_read_b64_tr_b8 and serves every head tile; P is
+//     rounded to f16.  528-byte rows: group scales multiply the QK partial
+//     sums per 128-wide group and, in PV, multiply P (normalised per tile by
+//     the largest scale, the factor applied to the tile's f32 product);
 //   epilogue: normalised output + lse, or (several splits) unnormalised
 //     partial (o, m, l) states that a second kernel merges.
 //
-// Workgroups of one unit are numbered b = 8k + x with the same x, so with the
+// All workgroups of one token are numbered b = 8k + (t mod 8), so with the
 // round-robin workgroup-to-XCD dispatch they share one XCD's L2.
 //
 // MFMA operand layouts (c = lane % 16, g = lane / 16): A (16 x K): lane (c, g)
 // holds row c; B (K x 16): lane (c, g) holds column c; for a given g and
 // register slot both hold the same reduction index, which is all a
-// contraction needs, so the reduction index is assigned freely: dims
-// kk*32 + g*8 + r for QK, entries ks*32 + g*8 + r for PV.  The 16x16 result:
-// lane (c, g) holds rows 4g..4g+3 of column c.
+// contraction needs, so the reduction index is assigned freely (dims for
+// QK, entries ks*32 + g*8 + r for PV).  The 16x16 result: lane (c, g) holds
+// rows 4g..4g+3 of column c.
 //
 // ds_read_b64_tr_b8 (measured on gfx950): within each 16-lane group, byte b
 // of lane l is byte (l & 7) of the 8 bytes addressed by lane 2b + (l >> 3).
@@ -60,9 +62,10 @@
 
 namespace dsa {
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kHB = 16;            // heads per workgroup
 constexpr int kTile = 64;          // entries per tile
 constexpr int kNBuf = 4;           // LDS tile buffers
 constexpr int kMaxSplit = 2048;    // entries per workgroup at most
@@ -72,20 +75,28 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;     // log2 headroom of the running max (P <= 256)
 
-// LDS map (bytes)
-constexpr int kBufBytes = kTile * 512;                  // 32 KB payload
-constexpr int kScBytes = kTile * 16;                    // 1 KB scales
-constexpr int kOffScales = kNBuf * kBufBytes;
-constexpr int kOffSlots = kOffScales + kNBuf * kScBytes;
-constexpr int kOffP = kOffSlots + kMaxSplit * 4;        // P, aliased with partial S
-constexpr int kPBytes = kWaves * kHB * 16 * 4;          // 8 KB
-constexpr int kOffRedM = kOffP + kPBytes;
-constexpr int kOffRedL = kOffRedM + kWaves * kHB * 4;
-constexpr int kLdsBytes = kOffRedL + kWaves * kHB * 4;
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-static_assert(kHB * kTile * 4 <= kPBytes, "P fits in the partial-S area");
+// LDS map (bytes) for NT head tiles of 16
+template <int NT>
+struct Lds {
+    static constexpr int kHB = 16 * NT;
+    static constexpr int kBufBytes = kTile * 512;                // 32 KB payload
+    static constexpr int kScBytes = kTile * 16;                  // 1 KB scales
+    static constexpr int kOffScales = kNBuf * kBufBytes;
+    static constexpr int kOffSlots = kOffScales + kNBuf * kScBytes;
+    static constexpr int kOffP = kOffSlots + kMaxSplit * 4;      // P, aliased with partial S
+    static constexpr int kPBytes = kWaves * kHB * 16 * 4;        // partial S of 8 waves
+    static constexpr int kOffRedM = kOffP + kPBytes;
+    static constexpr int kOffRedL = kOffRedM + kWaves * kHB * 4;
+    static constexpr int kBytes = kOffRedL + kWaves * kHB * 4;
+    static_assert(kBytes <= 160 * 1024, "LDS budget");
+    static_assert(kHB * kTile * 4 <= kPBytes, "P fits in the partial-S area");
+};
 
-__device__ __attribute__((aligned(16))) const uint8_t kZeroRow[kScaledBytes] = {};
+// Masked entries read zeros (P = 0 must never meet a NaN of an unreferenced
+// slot).  64 distinct zero rows, picked by the tile row, keep these reads off
+// a single set of L2 lines.
+constexpr int kZeroRows = 64;
+__device__ __attribute__((aligned(16))) const uint8_t kZeroRow[kZeroRows * kScaledBytes] = {};
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
@@ -150,13 +161,14 @@ __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_base) {
 // per instruction (lane l -> row 8w + 2k + (l >> 5), LDS chunk position
 // l & 31, holding global chunk (l & 31) ^ swz(row)); scaled rows add one
 // 8-lane instruction for the rows' 16-byte scale words.
-template <int LAYOUT>
+template <int LAYOUT, int NT>
 __device__ __forceinline__ void issue_tile(const AttnArgs &a, uint32_t lds0,
                                            const int32_t *slots, int tile_base,
                                            int buf, int w, int lane) {
+    using L = Lds<NT>;
     constexpr int64_t kRow = LAYOUT == 0 ? kRawBytes : kScaledBytes;
     const int r0 = kRowsPerWave * w;
-    const uint32_t dst = lds0 + buf * kBufBytes + r0 * 512;
+    const uint32_t dst = lds0 + buf * L::kBufBytes + r0 * 512;
     const int pos = lane & 31;
     int32_t sl[kLoadsRaw];
 #pragma unroll
@@ -166,21 +178,24 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, uint32_t lds0,
         const int r = r0 + 2 * k + (lane >> 5);
         const int chunk = pos ^ swz(r);
         const uint8_t *src = sl[k] >= 0 ? a.pool + (int64_t)sl[k] * kRow + chunk * 16
-                                        : kZeroRow + chunk * 16;
+                                        : kZeroRow + r * kRow + chunk * 16;
         dma16(src, dst + k * 1024);
     }
     if (LAYOUT == 1) {
         if (lane < kRowsPerWave) {
             const int r = r0 + lane;
             const int32_t slot = slots[tile_base + r];
-            const uint8_t *src = slot >= 0 ? a.pool + (int64_t)slot * kRow + kD : kZeroRow;
-            dma16(src, lds0 + kOffScales + buf * kScBytes + r0 * 16);
+            const uint8_t *src = slot >= 0 ? a.pool + (int64_t)slot * kRow + kD
+                                           : kZeroRow + r * kRow + kD;
+            dma16(src, lds0 + L::kOffScales + buf * L::kScBytes + r0 * 16);
         }
     }
 }
 
-template <int LAYOUT, bool QFP8, bool OUT_BF16, bool SPLIT>
+template <int LAYOUT, bool QFP8, bool OUT_BF16, bool SPLIT, int NT>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
+    using L = Lds<NT>;
+    constexpr int kHB = L::kHB;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int kLoads = kLoadsRaw + (LAYOUT == 1 ? 1 : 0);
     const int tid = threadIdx.x, lane = tid & 63;
@@ -189,24 +204,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int wq = w & 3;           // QK: entries 16 wq .. +16 of the tile
     const int hq = w >> 2;          // QK: dims half hq (256 dims)
     const int n_hb = (a.H + kHB - 1) / kHB;
-    const int units = a.T * n_hb;
 
-    // XCD-aware numbering: unit u's splits are blocks 8k + (u % 8)
+    // XCD-aware numbering: all of token t's workgroups are 8k + (t % 8)
+    const int per_tok = n_hb * a.n_splits;
     const int x = blockIdx.x & 7;
     const int kq = blockIdx.x >> 3;
+    const int t = (kq / per_tok) * 8 + x;
+    if (t >= a.T) return;
+    const int hb = (kq % per_tok) / a.n_splits;
     const int split = kq % a.n_splits;
-    const int unit = (kq / a.n_splits) * 8 + x;
-    if (unit >= units) return;
-    const int hb = unit % n_hb;
-    const int t = unit / n_hb;
-    const int h = hb * kHB + c;
-    const bool h_ok = h < a.H;
 
-    int32_t *slots = reinterpret_cast<int32_t *>(lds + kOffSlots);
-    float *p_lds = reinterpret_cast<float *>(lds + kOffP);    // [16 heads][64 entries]
-    float *sp_lds = reinterpret_cast<float *>(lds + kOffP);   // [8 waves][16 heads][16 entries]
-    float *red_m = reinterpret_cast<float *>(lds + kOffRedM);
-    float *red_l = reinterpret_cast<float *>(lds + kOffRedL);
+    int32_t *slots = reinterpret_cast<int32_t *>(lds + L::kOffSlots);
+    float *p_lds = reinterpret_cast<float *>(lds + L::kOffP);    // [kHB heads][64 entries]
+    float *sp_lds = reinterpret_cast<float *>(lds + L::kOffP);   // [8 waves][kHB heads][16]
+    float *red_m = reinterpret_cast<float *>(lds + L::kOffRedM);
+    float *red_l = reinterpret_cast<float *>(lds + L::kOffRedL);
 
     const int seq = a.token_seq ? a.token_seq[t] : t;
     const bool seq_ok = (a.page_table == nullptr && a.seq_lens == nullptr) ||
@@ -216,50 +228,82 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int n_ent = min(a.K - begin, a.split_len);   // a multiple of 64
     const int n_tiles = n_ent / kTile;
 
-    // Query of head c, dims half hq, as the B operand:
-    // bq[kk] = q[h][(8 hq + kk)*32 + g*8 .. +8].
-    bf16x8 bq[8];
+    // Query of head nt*16 + c as the B operand.  bf16: bq[nt][kk] =
+    // q[h][hq*256 + kk*32 + g*8 .. +8]; FP8: bq8[nt][k2] = q8[h][hq*256 +
+    // k2*128 + g*32 .. +32].  Heads beyond H read head 0 and are not stored.
+    bf16x8 bq[QFP8 ? 1 : NT][8];
+    i32x8 bq8[QFP8 ? NT : 1][2];
     float sscale = a.softmax_scale * kLog2e;
-    if (QFP8) {
+    if constexpr (QFP8) {
         sscale *= *a.q_scale;
-        const uint8_t *qp = reinterpret_cast<const uint8_t *>(a.q) +
-                            ((int64_t)t * a.H + (h_ok ? h : 0)) * kD + hq * 256 + g * 8;
 #pragma unroll
-        for (int kk = 0; kk < 8; kk++) {
-            u32x2 v = h_ok ? *reinterpret_cast<const u32x2 *>(qp + kk * 32) : u32x2{0, 0};
-            bq[kk] = e4m3x8_to_bf16(v[0], v[1]);
+        for (int nt = 0; nt < NT; nt++) {
+            const int h = hb * kHB + nt * 16 + c;
+            const uint8_t *qp = reinterpret_cast<const uint8_t *>(a.q) +
+                                ((int64_t)t * a.H + (h < a.H ? h : 0)) * kD + hq * 256 + g * 32;
+#pragma unroll
+            for (int k2 = 0; k2 < 2; k2++)
+                bq8[nt][k2] = *reinterpret_cast<const i32x8 *>(qp + k2 * 128);
         }
     } else {
-        const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) +
-                           ((int64_t)t * a.H + (h_ok ? h : 0)) * kD + hq * 256 + g * 8;
 #pragma unroll
-        for (int kk = 0; kk < 8; kk++) {
-            u32x4 v = h_ok ? *reinterpret_cast<const u32x4 *>(qp + kk * 32)
-                           : u32x4{0, 0, 0, 0};
-            bq[kk] = __builtin_bit_cast(bf16x8, v);
+        for (int nt = 0; nt < NT; nt++) {
+            const int h = hb * kHB + nt * 16 + c;
+            const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) +
+                               ((int64_t)t * a.H + (h < a.H ? h : 0)) * kD + hq * 256 + g * 8;
+#pragma unroll
+            for (int kk = 0; kk < 8; kk++)
+                bq[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qp + kk * 32));
         }
     }
+
     // ---- prologue: resolve this split's indices into LDS.  Every load is
     // unconditional (addresses clamped into range, results selected after),
-    // so each phase issues all its loads before a single wait.
+    // so each phase issues all its loads before a single wait.  When the
+    // token's page-table row fits in the (still unused) P area it is staged
+    // there together with the top-k loads, so resolution costs one global
+    // latency instead of two.
     {
         constexpr int kPer = kMaxSplit / kThreads;
+        constexpr int kPtCap = L::kPBytes / 4;
+        constexpr int kPtPer = kPtCap / kThreads;
         const int32_t *tk = a.topk + (int64_t)t * a.K + begin;
+        const int32_t *row = a.page_table + (int64_t)(seq_ok ? seq : 0) * a.max_pages;
+        int32_t *pt_lds = reinterpret_cast<int32_t *>(lds + L::kOffP);
+        const bool pt_staged = a.page_table != nullptr && a.max_pages <= kPtCap;
         int32_t v[kPer], phys[kPer];
+        if (pt_staged) {
+            int32_t pw[kPtPer];
 #pragma unroll
-        for (int i = 0; i < kPer; i++) {
-            const int j = tid + i * kThreads;
-            const int32_t x = tk[min(j, n_ent - 1)];
-            v[i] = j < n_ent ? x : -1;
-        }
-        if (a.page_table) {
-            const int32_t *row = a.page_table + (int64_t)(seq_ok ? seq : 0) * a.max_pages;
+            for (int k = 0; k < kPtPer; k++) pw[k] = row[min(tid + k * kThreads, a.max_pages - 1)];
+#pragma unroll
+            for (int i = 0; i < kPer; i++) {
+                const int j = tid + i * kThreads;
+                const int32_t xv = tk[min(j, n_ent - 1)];
+                v[i] = j < n_ent ? xv : -1;
+            }
+#pragma unroll
+            for (int k = 0; k < kPtPer; k++)
+                if (tid + k * kThreads < a.max_pages) pt_lds[tid + k * kThreads] = pw[k];
+            __syncthreads();
 #pragma unroll
             for (int i = 0; i < kPer; i++)
-                phys[i] = row[min(max(v[i], 0) >> a.page_shift, a.max_pages - 1)];
+                phys[i] = pt_lds[min(max(v[i], 0) >> a.page_shift, a.max_pages - 1)];
         } else {
 #pragma unroll
-            for (int i = 0; i < kPer; i++) phys[i] = 0;
+            for (int i = 0; i < kPer; i++) {
+                const int j = tid + i * kThreads;
+                const int32_t xv = tk[min(j, n_ent - 1)];
+                v[i] = j < n_ent ? xv : -1;
+            }
+            if (a.page_table) {
+#pragma unroll
+                for (int i = 0; i < kPer; i++)
+                    phys[i] = row[min(max(v[i], 0) >> a.page_shift, a.max_pages - 1)];
+            } else {
+#pragma unroll
+                for (int i = 0; i < kPer; i++) phys[i] = 0;
+            }
         }
         int n_err = 0;
 #pragma unroll
@@ -284,17 +328,22 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // ---- fill the pipeline
 #pragma unroll
     for (int i = 0; i < kNBuf - 1; i++)
-        if (i < n_tiles) issue_tile<LAYOUT>(a, lds0, slots, i * kTile, i, w, lane);
+        if (i < n_tiles) issue_tile<LAYOUT, NT>(a, lds0, slots, i * kTile, i, w, lane);
 
-    float m_run = -INFINITY, l_part = 0.0f;
-    f32x4 acc[4];
+    float m_run[NT], l_part[NT];
+    f32x4 acc[4][NT];
 #pragma unroll
-    for (int dt = 0; dt < 4; dt++) acc[dt] = f32x4{0, 0, 0, 0};
+    for (int nt = 0; nt < NT; nt++) {
+        m_run[nt] = -INFINITY;
+        l_part[nt] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) acc[dt][nt] = f32x4{0, 0, 0, 0};
+    }
 
     for (int it = 0; it < n_tiles; it++) {
         const int buf = it % kNBuf;
-        const uint8_t *xb = lds + buf * kBufBytes;
-        const f32x4 *scb = reinterpret_cast<const f32x4 *>(lds + kOffScales + buf * kScBytes);
+        const uint8_t *xb = lds + buf * L::kBufBytes;
+        const f32x4 *scb = reinterpret_cast<const f32x4 *>(lds + L::kOffScales + buf * L::kScBytes);
         const int32_t *ts = slots + it * kTile;
 
         // (A) this tile's rows have landed (for this wave), then for all
@@ -304,63 +353,108 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         else wait_vm_lgkm0<0>();
         barrier_raw();
         if (it + kNBuf - 1 < n_tiles)
-            issue_tile<LAYOUT>(a, lds0, slots, (it + kNBuf - 1) * kTile,
-                               (it + kNBuf - 1) % kNBuf, w, lane);
+            issue_tile<LAYOUT, NT>(a, lds0, slots, (it + kNBuf - 1) * kTile,
+                                   (it + kNBuf - 1) % kNBuf, w, lane);
 
         // (B) partial S^T for entries 16 wq .. +16 over dims half hq
         {
             const int r = 16 * wq + c;
-            const uint8_t *xr = xb + r * 512 + (g & 1) * 8;
+            const uint8_t *xr = xb + r * 512;
             const int sw = swz(r);
-            u32x2 xa[8];
-#pragma unroll
-            for (int kk = 0; kk < 8; kk++)
-                xa[kk] = *reinterpret_cast<const u32x2 *>(
-                    xr + ((((8 * hq + kk) * 2 + (g >> 1)) ^ sw) * 16));
             f32x4 sc4[4];
             if constexpr (LAYOUT == 1) {
 #pragma unroll
                 for (int i = 0; i < 4; i++) sc4[i] = scb[16 * wq + 4 * g + i];
             }
-            f32x4 accg[2];
-            accg[0] = accg[1] = f32x4{0, 0, 0, 0};
+            f32x4 part[NT];
+            if constexpr (QFP8) {
+                // 2 steps of K = 128: dims hq*256 + k2*128 + g*32 .. +32 (two
+                // 16-byte chunks); each step is exactly one scale group
+                u32x4 xa[2][2];
 #pragma unroll
-            for (int kk = 0; kk < 8; kk++) {
-                const bf16x8 av = e4m3x8_to_bf16(xa[kk][0], xa[kk][1]);
-                // raw rows: two independent chains (even / odd kk); scaled
-                // rows: one chain per 128-wide scale group of this half
-                const int q = LAYOUT == 0 ? (kk & 1) : (kk >> 2);
-                accg[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[kk], accg[q], 0, 0, 0);
-            }
-            f32x4 part;
+                for (int k2 = 0; k2 < 2; k2++)
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                if constexpr (LAYOUT == 0)
-                    part[i] = accg[0][i] + accg[1][i];
-                else
-                    part[i] = accg[0][i] * sc4[i][2 * hq] + accg[1][i] * sc4[i][2 * hq + 1];
+                    for (int hf = 0; hf < 2; hf++)
+                        xa[k2][hf] = *reinterpret_cast<const u32x4 *>(
+                            xr + (((hq * 16 + k2 * 8 + g * 2 + hf) ^ sw) * 16));
+#pragma unroll
+                for (int nt = 0; nt < NT; nt++) {
+                    f32x4 accg[2];
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; k2++) {
+                        const i32x8 av = {(int)xa[k2][0][0], (int)xa[k2][0][1], (int)xa[k2][0][2],
+                                          (int)xa[k2][0][3], (int)xa[k2][1][0], (int)xa[k2][1][1],
+                                          (int)xa[k2][1][2], (int)xa[k2][1][3]};
+                        accg[k2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            av, bq8[nt][k2], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        if constexpr (LAYOUT == 0)
+                            part[nt][i] = accg[0][i] + accg[1][i];
+                        else
+                            part[nt][i] = accg[0][i] * sc4[i][2 * hq] + accg[1][i] * sc4[i][2 * hq + 1];
+                    }
+                }
+            } else {
+                // 8 steps of K = 32: dims hq*256 + kk*32 + g*8 .. +8
+                u32x2 xa[8];
+#pragma unroll
+                for (int kk = 0; kk < 8; kk++)
+                    xa[kk] = *reinterpret_cast<const u32x2 *>(
+                        xr + ((((8 * hq + kk) * 2 + (g >> 1)) ^ sw) * 16) + (g & 1) * 8);
+                f32x4 accg[NT][2];
+#pragma unroll
+                for (int nt = 0; nt < NT; nt++) accg[nt][0] = accg[nt][1] = f32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int kk = 0; kk < 8; kk++) {
+                    const bf16x8 av = e4m3x8_to_bf16(xa[kk][0], xa[kk][1]);
+                    // raw rows: two independent chains (even / odd kk); scaled
+                    // rows: one chain per 128-wide scale group of this half
+                    const int q = LAYOUT == 0 ? (kk & 1) : (kk >> 2);
+#pragma unroll
+                    for (int nt = 0; nt < NT; nt++)
+                        accg[nt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[nt][kk],
+                                                                              accg[nt][q], 0, 0, 0);
+                }
+#pragma unroll
+                for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        if constexpr (LAYOUT == 0)
+                            part[nt][i] = accg[nt][0][i] + accg[nt][1][i];
+                        else
+                            part[nt][i] = accg[nt][0][i] * sc4[i][2 * hq] +
+                                          accg[nt][1][i] * sc4[i][2 * hq + 1];
+                    }
             }
-            *reinterpret_cast<f32x4 *>(sp_lds + (w * kHB + c) * 16 + 4 * g) = part;
+#pragma unroll
+            for (int nt = 0; nt < NT; nt++)
+                *reinterpret_cast<f32x4 *>(sp_lds + (w * kHB + nt * 16 + c) * 16 + 4 * g) = part[nt];
         }
         wait_lgkm0();
         barrier_raw();
 
-        // (C) full scores of entries 16 wq + 4g + i, head c; tile max
-        float sv[4];
+        // (C) full scores of entries 16 wq + 4g + i, heads nt*16 + c; tile max
+        float sv[NT][4];
         {
-            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sp_lds + (wq * kHB + c) * 16 + 4 * g);
-            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sp_lds + ((wq + 4) * kHB + c) * 16 + 4 * g);
             const int4 sl4 = *reinterpret_cast<const int4 *>(ts + 16 * wq + 4 * g);
             const int slv[4] = {sl4.x, sl4.y, sl4.z, sl4.w};
-            float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                sv[i] = slv[i] >= 0 ? (s0[i] + s1[i]) * sscale : -INFINITY;
-                mx = fmaxf(mx, sv[i]);
+            for (int nt = 0; nt < NT; nt++) {
+                const int hh = nt * 16 + c;
+                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sp_lds + (wq * kHB + hh) * 16 + 4 * g);
+                const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sp_lds + ((wq + 4) * kHB + hh) * 16 + 4 * g);
+                float mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    sv[nt][i] = slv[i] >= 0 ? (s0[i] + s1[i]) * sscale : -INFINITY;
+                    mx = fmaxf(mx, sv[nt][i]);
+                }
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                if (g == 0 && w < 4) red_m[w * kHB + hh] = mx;
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            if (g == 0 && w < 4) red_m[w * kHB + c] = mx;
         }
         wait_lgkm0();
         barrier_raw();
@@ -371,25 +465,34 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         // All waves see the same maxima and so make the same choice.  Waves
         // 0-3 own the entries' P and their share of the denominator.
         {
-            const float tmax = fmaxf(fmaxf(red_m[c], red_m[kHB + c]),
-                                     fmaxf(red_m[2 * kHB + c], red_m[3 * kHB + c]));
-            const bool resc = tmax - m_run > kSlack;   // false when both are -inf
-            const float alpha = resc ? exp2f(m_run - tmax) : 1.0f;
-            if (resc) m_run = tmax;
-            if (w < 4) {
-                f32x4 p;
-                float ps = 0.0f;
+            bool any_resc = false;
+            float alpha[NT];
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    p[i] = sv[i] == -INFINITY ? 0.0f : exp2f(sv[i] - m_run);
-                    ps += p[i];
+            for (int nt = 0; nt < NT; nt++) {
+                const int hh = nt * 16 + c;
+                const float tmax = fmaxf(fmaxf(red_m[hh], red_m[kHB + hh]),
+                                         fmaxf(red_m[2 * kHB + hh], red_m[3 * kHB + hh]));
+                const bool resc = tmax - m_run[nt] > kSlack;   // false when both are -inf
+                alpha[nt] = resc ? exp2f(m_run[nt] - tmax) : 1.0f;
+                if (resc) m_run[nt] = tmax;
+                any_resc |= resc;
+                if (w < 4) {
+                    f32x4 p;
+                    float ps = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        p[i] = sv[nt][i] == -INFINITY ? 0.0f : exp2f(sv[nt][i] - m_run[nt]);
+                        ps += p[i];
+                    }
+                    l_part[nt] = l_part[nt] * alpha[nt] + ps;
+                    *reinterpret_cast<f32x4 *>(p_lds + hh * kTile + 16 * w + 4 * g) = p;
                 }
-                l_part = l_part * alpha + ps;
-                *reinterpret_cast<f32x4 *>(p_lds + c * kTile + 16 * w + 4 * g) = p;
             }
-            if (__ballot(resc)) {
+            if (__ballot(any_resc)) {
 #pragma unroll
-                for (int dt = 0; dt < 4; dt++) acc[dt] *= alpha;
+                for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+                    for (int dt = 0; dt < 4; dt++) acc[dt][nt] *= alpha[nt];
             }
         }
         wait_lgkm0();
@@ -397,13 +500,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 
         // (E) O^T[dims 64w.., heads] += X^T . P^T over the 64 entries.
         {
-            // B operand P^T: entries ks*32 + g*8 + r of head c
-            f32x4 pr[4];
-#pragma unroll
-            for (int ks = 0; ks < 2; ks++) {
-                pr[2 * ks] = *reinterpret_cast<const f32x4 *>(p_lds + c * kTile + ks * 32 + g * 8);
-                pr[2 * ks + 1] = *reinterpret_cast<const f32x4 *>(p_lds + c * kTile + ks * 32 + g * 8 + 4);
-            }
             // A operand X^T via transpose reads: lane (c, g) addresses entry
             // e0 + (c >> 1), half (c & 1) of the chunk of dims 64w + 16dt ..
             u32x2 tv[2][4];
@@ -418,13 +514,20 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                         u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_i32x2 *>(
                                    LDS_PTR(rp + (((4 * w + dt) ^ sw) * 16)))));
             }
-            float pv[2][8];
+            // B operand P^T: entries ks*32 + g*8 + r of head nt*16 + c
+            float pv[NT][2][8];
 #pragma unroll
-            for (int ks = 0; ks < 2; ks++)
+            for (int nt = 0; nt < NT; nt++)
 #pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    pv[ks][r] = pr[2 * ks][r];
-                    pv[ks][4 + r] = pr[2 * ks + 1][r];
+                for (int ks = 0; ks < 2; ks++) {
+                    const float *pp = p_lds + (nt * 16 + c) * kTile + ks * 32 + g * 8;
+                    const f32x4 p0 = *reinterpret_cast<const f32x4 *>(pp);
+                    const f32x4 p1 = *reinterpret_cast<const f32x4 *>(pp + 4);
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        pv[nt][ks][r] = p0[r];
+                        pv[nt][ks][4 + r] = p1[r];
+                    }
                 }
             float smax = 1.0f;
             if constexpr (LAYOUT == 1) {
@@ -446,69 +549,80 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 smax = fmaxf(smax, __shfl_xor(smax, 32));
                 const float inv = smax > 0.0f ? 1.0f / smax : 0.0f;
 #pragma unroll
+                for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+                        for (int r = 0; r < 8; r++) pv[nt][ks][r] *= sc[ks][r] * inv;
+            }
+            f16x8 bp[NT][2];
+#pragma unroll
+            for (int nt = 0; nt < NT; nt++)
+#pragma unroll
                 for (int ks = 0; ks < 2; ks++)
 #pragma unroll
-                    for (int r = 0; r < 8; r++) pv[ks][r] *= sc[ks][r] * inv;
-            }
-            f16x8 bp[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ks++)
-#pragma unroll
-                for (int r = 0; r < 8; r++) bp[ks][r] = (_Float16)pv[ks][r];
+                    for (int r = 0; r < 8; r++) bp[nt][ks][r] = (_Float16)pv[nt][ks][r];
 #pragma unroll
             for (int dt = 0; dt < 4; dt++) {
-                if constexpr (LAYOUT == 0) {
+                const f16x8 av0 = e4m3x8_to_f16(tv[0][dt][0], tv[0][dt][1]);
+                const f16x8 av1 = e4m3x8_to_f16(tv[1][dt][0], tv[1][dt][1]);
 #pragma unroll
-                    for (int ks = 0; ks < 2; ks++)
-                        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            e4m3x8_to_f16(tv[ks][dt][0], tv[ks][dt][1]), bp[ks], acc[dt], 0, 0, 0);
-                } else {
-                    f32x4 part = {0, 0, 0, 0};
-#pragma unroll
-                    for (int ks = 0; ks < 2; ks++)
-                        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            e4m3x8_to_f16(tv[ks][dt][0], tv[ks][dt][1]), bp[ks], part, 0, 0, 0);
-                    acc[dt] += part * smax;
+                for (int nt = 0; nt < NT; nt++) {
+                    if constexpr (LAYOUT == 0) {
+                        acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, bp[nt][0], acc[dt][nt], 0, 0, 0);
+                        acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bp[nt][1], acc[dt][nt], 0, 0, 0);
+                    } else {
+                        f32x4 prt = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, bp[nt][0], f32x4{0, 0, 0, 0}, 0, 0, 0);
+                        prt = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bp[nt][1], prt, 0, 0, 0);
+                        acc[dt][nt] += prt * smax;
+                    }
                 }
             }
         }
     }
 
     // total softmax denominator per head: lanes of this wave, then waves 0-3
-    l_part += __shfl_xor(l_part, 16);
-    l_part += __shfl_xor(l_part, 32);
-    if (g == 0 && w < 4) red_l[w * kHB + c] = l_part;
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) {
+        l_part[nt] += __shfl_xor(l_part[nt], 16);
+        l_part[nt] += __shfl_xor(l_part[nt], 32);
+        if (g == 0 && w < 4) red_l[w * kHB + nt * 16 + c] = l_part[nt];
+    }
     __syncthreads();
-    const float l_tot = red_l[c] + red_l[kHB + c] + red_l[2 * kHB + c] + red_l[3 * kHB + c];
-    if (!h_ok) return;
-
-    const int64_t th = (int64_t)t * a.H + h;
-    if (SPLIT) {
-        float *wo = a.ws + (th * a.n_splits + split) * kD + 64 * w + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < 4; dt++) *reinterpret_cast<f32x4 *>(wo + dt * 16) = acc[dt];
-        if (w == 0 && g == 0) {
-            float *ml = a.ws + (int64_t)a.T * a.H * a.n_splits * kD +
-                        (th * a.n_splits + split) * 2;
-            ml[0] = m_run;
-            ml[1] = l_tot;
-        }
-    } else {
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        const int64_t base = th * kD + 64 * w + 4 * g;
+    for (int nt = 0; nt < NT; nt++) {
+        const int hh = nt * 16 + c;
+        const int h = hb * kHB + hh;
+        if (h >= a.H) continue;
+        const float l_tot = red_l[hh] + red_l[kHB + hh] + red_l[2 * kHB + hh] + red_l[3 * kHB + hh];
+        const int64_t th = (int64_t)t * a.H + h;
+        if (SPLIT) {
+            float *wo = a.ws + (th * a.n_splits + split) * kD + 64 * w + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < 4; dt++) {
-            const f32x4 o = acc[dt] * inv;
-            if (OUT_BF16) {
-                u32x2 pk = {f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
-                            f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16)};
-                *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + base + dt * 16) = pk;
-            } else {
-                *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + base + dt * 16) = o;
+            for (int dt = 0; dt < 4; dt++) *reinterpret_cast<f32x4 *>(wo + dt * 16) = acc[dt][nt];
+            if (w == 0 && g == 0) {
+                float *ml = a.ws + (int64_t)a.T * a.H * a.n_splits * kD +
+                            (th * a.n_splits + split) * 2;
+                ml[0] = m_run[nt];
+                ml[1] = l_tot;
             }
+        } else {
+            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            const int64_t base = th * kD + 64 * w + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < 4; dt++) {
+                const f32x4 o = acc[dt][nt] * inv;
+                if (OUT_BF16) {
+                    u32x2 pk = {f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
+                                f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16)};
+                    *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + base + dt * 16) = pk;
+                } else {
+                    *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + base + dt * 16) = o;
+                }
+            }
+            if (a.lse && w == 0 && g == 0)
+                a.lse[th] = l_tot > 0.0f ? (m_run[nt] + log2f(l_tot)) * kLn2 : -INFINITY;
         }
-        if (a.lse && w == 0 && g == 0)
-            a.lse[th] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     }
 }
 
@@ -524,13 +638,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     float M = -INFINITY;
     for (int s = 0; s < S; s++) M = fmaxf(M, ml[2 * s]);
     float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    float L = 0.0f;
+    float Lsum = 0.0f;
     if (M != -INFINITY) {
         for (int s = 0; s < S; s++) {
             const float ms = ml[2 * s];
             if (ms == -INFINITY) continue;
             const float wgt = exp2f(ms - M);
-            L += wgt * ml[2 * s + 1];
+            Lsum += wgt * ml[2 * s + 1];
             const float *src = a.ws + (th * S + s) * kD + lane * 8;
             const f32x4 v0 = *reinterpret_cast<const f32x4 *>(src);
             const f32x4 v1 = *reinterpret_cast<const f32x4 *>(src + 4);
@@ -541,7 +655,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
             }
         }
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
     if (OUT_BF16) {
         u32x4 pk;
 #pragma unroll
@@ -553,13 +667,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
         *reinterpret_cast<f32x4 *>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
         *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
     }
-    if (a.lse && lane == 0) a.lse[th] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    if (a.lse && lane == 0) a.lse[th] = Lsum > 0.0f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
 }
+
+// Heads per workgroup: 32 when there are more than 16 heads (a row is then
+// gathered once per 32 heads), else 16.
+static int head_tiles(int H) { return H > 16 ? 2 : 1; }
 
 // Splits per (token, head block): enough workgroups to cover the CUs for
 // small batches, and never more than kMaxSplit entries per workgroup.
 int attn_decode_splits(int T, int H, int K) {
-    const int64_t units = (int64_t)T * ((H + kHB - 1) / kHB);
+    const int hbw = 16 * head_tiles(H);
+    const int64_t units = (int64_t)T * ((H + hbw - 1) / hbw);
     const int tiles = K / kTile;
     if (units <= 0 || tiles <= 0) return 1;
     int64_t s = (DSA_DECODE_TARGET_BLOCKS + units - 1) / units;
@@ -588,31 +707,38 @@ size_t attn_workspace_bytes(int T, int H, int K, int phase) {
     return (b + 255) & ~(size_t)255;
 }
 
-template <typename K>
-static void allow_big_lds(K kern) {
+template <typename Kern>
+static void allow_big_lds(Kern kern, int bytes) {
     // once per instantiation; not a stream operation, so capture-safe
     static const hipError_t e = hipFuncSetAttribute(
-        (const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        (const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     (void)e;
 }
 
-template <int LAYOUT, bool QFP8, bool OUT_BF16>
+template <int LAYOUT, bool QFP8, bool OUT_BF16, int NT>
 static hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
+    constexpr int kHB = 16 * NT;
     const int n_hb = (a.H + kHB - 1) / kHB;
-    const int64_t units = (int64_t)a.T * n_hb;
-    const dim3 grid((unsigned)(((units + 7) / 8) * 8 * a.n_splits));
+    const dim3 grid((unsigned)(((int64_t)a.T + 7) / 8 * 8 * n_hb * a.n_splits));
+    constexpr int bytes = Lds<NT>::kBytes;
     if (a.n_splits > 1) {
-        auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, true>;
-        allow_big_lds(kern);
-        kern<<<grid, dim3(kThreads), kLdsBytes, stream>>>(a);
+        auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, true, NT>;
+        allow_big_lds(kern, bytes);
+        kern<<<grid, dim3(kThreads), bytes, stream>>>(a);
         const dim3 cgrid((unsigned)(((int64_t)a.T * a.H + 3) / 4));
         attn_combine_kernel<OUT_BF16><<<cgrid, dim3(256), 0, stream>>>(a);
     } else {
-        auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, false>;
-        allow_big_lds(kern);
-        kern<<<grid, dim3(kThreads), kLdsBytes, stream>>>(a);
+        auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, false, NT>;
+        allow_big_lds(kern, bytes);
+        kern<<<grid, dim3(kThreads), bytes, stream>>>(a);
     }
     return hipGetLastError();
+}
+
+template <int LAYOUT, bool QFP8, bool OUT_BF16>
+static hipError_t launch_nt(const AttnArgs &a, hipStream_t stream) {
+    return head_tiles(a.H) == 2 ? launch_one<LAYOUT, QFP8, OUT_BF16, 2>(a, stream)
+                                : launch_one<LAYOUT, QFP8, OUT_BF16, 1>(a, stream);
 }
 
 hipError_t launch_attn(const AttnArgs &a_in, int layout, bool q_fp8, bool out_bf16,
@@ -621,7 +747,7 @@ hipError_t launch_attn(const AttnArgs &a_in, int layout, bool q_fp8, bool out_bf
     if (a.n_splits < 1) a.n_splits = 1;
     a.split_len = split_len_for(a.K, a.n_splits);
 #define DSA_DISPATCH(L, Q, O) \
-    if (layout == L && q_fp8 == Q && out_bf16 == O) return launch_one<L, Q, O>(a, stream);
+    if (layout == L && q_fp8 == Q && out_bf16 == O) return launch_nt<L, Q, O>(a, stream);
     DSA_DISPATCH(0, false, false)
     DSA_DISPATCH(0, false, true)
     DSA_DISPATCH(0, true, false)
