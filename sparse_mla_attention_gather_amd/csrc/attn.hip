@@ -74,6 +74,9 @@ constexpr int kLoadsRaw = kRowsPerWave / 2;         // DMA instructions per wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;     // log2 headroom of the running max (P <= 256)
+// "No maximum yet": finite, so that 2^(-inf - kNoMax) = 0 for masked scores
+// without a select, and far below any real score.
+constexpr float kNoMax = -1.0e30f;
 
 // LDS map (bytes) for NT head tiles of 16
 template <int NT>
@@ -138,6 +141,13 @@ __device__ __forceinline__ int32_t resolve_entry(const AttnArgs &a, int32_t i,
 }
 
 __device__ __forceinline__ int swz(int row) { return row & 7; }
+
+// LDS slot swizzles that keep eight consecutive lanes c of a 16-byte access
+// on distinct banks: the partial-score rows ([head][4 entry groups]) rotate
+// their groups by (c & 7) >> 1, the P rows ([head][16 groups of 4 entries])
+// XOR their group index with c & 7.
+__device__ __forceinline__ int sp_slot(int grp, int c) { return (grp + ((c & 7) >> 1)) & 3; }
+__device__ __forceinline__ int p_slot(int grp, int c) { return grp ^ (c & 7); }
 
 // 32-bit LDS address of a pointer into dynamic shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -228,9 +238,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int n_ent = min(a.K - begin, a.split_len);   // a multiple of 64
     const int n_tiles = n_ent / kTile;
 
-    // Query of head nt*16 + c as the B operand.  bf16: bq[nt][kk] =
-    // q[h][hq*256 + kk*32 + g*8 .. +8]; FP8: bq8[nt][k2] = q8[h][hq*256 +
-    // k2*128 + g*32 .. +32].  Heads beyond H read head 0 and are not stored.
+    // Query of head nt*16 + c as the B operand.  bf16: bq[nt][kk] = q[h][d ..
+    // d+8] with d = (hq*16 + (kk>>1)*4 + g)*16 + (kk&1)*8, so that a lane's
+    // two steps 2m, 2m+1 use one 16-byte chunk of the row; FP8: bq8[nt][k2] =
+    // q8[h][hq*256 + k2*128 + g*32 .. +32].  Heads beyond H read head 0 and
+    // are not stored.
     bf16x8 bq[QFP8 ? 1 : NT][8];
     i32x8 bq8[QFP8 ? NT : 1][2];
     float sscale = a.softmax_scale * kLog2e;
@@ -250,10 +262,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         for (int nt = 0; nt < NT; nt++) {
             const int h = hb * kHB + nt * 16 + c;
             const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) +
-                               ((int64_t)t * a.H + (h < a.H ? h : 0)) * kD + hq * 256 + g * 8;
+                               ((int64_t)t * a.H + (h < a.H ? h : 0)) * kD;
 #pragma unroll
             for (int kk = 0; kk < 8; kk++)
-                bq[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qp + kk * 32));
+                bq[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+                    qp + (hq * 16 + (kk >> 1) * 4 + g) * 16 + (kk & 1) * 8));
         }
     }
 
@@ -334,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     f32x4 acc[4][NT];
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) {
-        m_run[nt] = -INFINITY;
+        m_run[nt] = kNoMax;
         l_part[nt] = 0.0f;
 #pragma unroll
         for (int dt = 0; dt < 4; dt++) acc[dt][nt] = f32x4{0, 0, 0, 0};
@@ -397,18 +410,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                     }
                 }
             } else {
-                // 8 steps of K = 32: dims hq*256 + kk*32 + g*8 .. +8
-                u32x2 xa[8];
+                // 8 steps of K = 32; steps 2m, 2m+1 take the two halves of
+                // chunk hq*16 + 4m + g (so a step's 32 dims stay inside one
+                // 128-wide scale group: group 2hq + m/2)
+                u32x4 xc[4];
 #pragma unroll
-                for (int kk = 0; kk < 8; kk++)
-                    xa[kk] = *reinterpret_cast<const u32x2 *>(
-                        xr + ((((8 * hq + kk) * 2 + (g >> 1)) ^ sw) * 16) + (g & 1) * 8);
+                for (int m = 0; m < 4; m++)
+                    xc[m] = *reinterpret_cast<const u32x4 *>(xr + (((hq * 16 + m * 4 + g) ^ sw) * 16));
                 f32x4 accg[NT][2];
 #pragma unroll
                 for (int nt = 0; nt < NT; nt++) accg[nt][0] = accg[nt][1] = f32x4{0, 0, 0, 0};
 #pragma unroll
                 for (int kk = 0; kk < 8; kk++) {
-                    const bf16x8 av = e4m3x8_to_bf16(xa[kk][0], xa[kk][1]);
+                    const u32x4 &ch = xc[kk >> 1];
+                    const bf16x8 av = (kk & 1) ? e4m3x8_to_bf16(ch[2], ch[3])
+                                               : e4m3x8_to_bf16(ch[0], ch[1]);
                     // raw rows: two independent chains (even / odd kk); scaled
                     // rows: one chain per 128-wide scale group of this half
                     const int q = LAYOUT == 0 ? (kk & 1) : (kk >> 2);
@@ -430,7 +446,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             }
 #pragma unroll
             for (int nt = 0; nt < NT; nt++)
-                *reinterpret_cast<f32x4 *>(sp_lds + (w * kHB + nt * 16 + c) * 16 + 4 * g) = part[nt];
+                *reinterpret_cast<f32x4 *>(sp_lds + (w * kHB + nt * 16 + c) * 16 +
+                                           4 * sp_slot(g, c)) = part[nt];
         }
         wait_lgkm0();
         barrier_raw();
@@ -443,8 +460,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int nt = 0; nt < NT; nt++) {
                 const int hh = nt * 16 + c;
-                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sp_lds + (wq * kHB + hh) * 16 + 4 * g);
-                const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sp_lds + ((wq + 4) * kHB + hh) * 16 + 4 * g);
+                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sp_lds + (wq * kHB + hh) * 16 + 4 * sp_slot(g, c));
+                const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sp_lds + ((wq + 4) * kHB + hh) * 16 + 4 * sp_slot(g, c));
                 float mx = -INFINITY;
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
@@ -472,8 +489,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 const int hh = nt * 16 + c;
                 const float tmax = fmaxf(fmaxf(red_m[hh], red_m[kHB + hh]),
                                          fmaxf(red_m[2 * kHB + hh], red_m[3 * kHB + hh]));
-                const bool resc = tmax - m_run[nt] > kSlack;   // false when both are -inf
-                alpha[nt] = resc ? exp2f(m_run[nt] - tmax) : 1.0f;
+                const bool resc = tmax - m_run[nt] > kSlack;   // false for an all-masked tile
+                alpha[nt] = resc ? __builtin_amdgcn_exp2f(m_run[nt] - tmax) : 1.0f;
                 if (resc) m_run[nt] = tmax;
                 any_resc |= resc;
                 if (w < 4) {
@@ -481,11 +498,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                     float ps = 0.0f;
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
-                        p[i] = sv[nt][i] == -INFINITY ? 0.0f : exp2f(sv[nt][i] - m_run[nt]);
+                        p[i] = __builtin_amdgcn_exp2f(sv[nt][i] - m_run[nt]);   // masked: 2^-inf = 0
                         ps += p[i];
                     }
                     l_part[nt] = l_part[nt] * alpha[nt] + ps;
-                    *reinterpret_cast<f32x4 *>(p_lds + hh * kTile + 16 * w + 4 * g) = p;
+                    *reinterpret_cast<f32x4 *>(p_lds + hh * kTile + 4 * p_slot(4 * w + g, c)) = p;
                 }
             }
             if (__ballot(any_resc)) {
@@ -520,9 +537,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             for (int nt = 0; nt < NT; nt++)
 #pragma unroll
                 for (int ks = 0; ks < 2; ks++) {
-                    const float *pp = p_lds + (nt * 16 + c) * kTile + ks * 32 + g * 8;
-                    const f32x4 p0 = *reinterpret_cast<const f32x4 *>(pp);
-                    const f32x4 p1 = *reinterpret_cast<const f32x4 *>(pp + 4);
+                    const float *pp = p_lds + (nt * 16 + c) * kTile;
+                    const f32x4 p0 = *reinterpret_cast<const f32x4 *>(pp + 4 * p_slot(ks * 8 + g * 2, c));
+                    const f32x4 p1 = *reinterpret_cast<const f32x4 *>(pp + 4 * p_slot(ks * 8 + g * 2 + 1, c));
 #pragma unroll
                     for (int r = 0; r < 4; r++) {
                         pv[nt][ks][r] = p0[r];
