@@ -32,6 +32,12 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with "
         "`python -m sparse_mla_attention_gather_amd.build` (hipcc, gfx950)")
 
+# PyTorch ships its own copy of the HIP runtime.  Loading it first makes this
+# library bind to that same runtime instance (one device context, one set of
+# streams); loaded the other way round, the process would hold two runtimes
+# and the library would not see torch's device state.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 _SIGS = {

@@ -124,7 +124,7 @@ int32_t run_attn(int32_t phase, const void *q, int32_t q_dtype,
     a.out = out;
     a.lse = lse;
     a.ws = static_cast<float *>(workspace);
-    a.n_splits = dsa::attn_splits(T, H, K, phase);
+    a.n_splits = dsa::attn_splits(T, H, K, phase, layout);
     a.split_len = 0;
     a.err_count = err_count;
     hipError_t e = dsa::launch_attn(a, layout, q_dtype == DSA_FP8_E4M3FN,

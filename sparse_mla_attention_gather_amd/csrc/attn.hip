@@ -7,35 +7,47 @@
 // and value.  out[t,h] = softmax_j(scale * <q[t,h], x_j>) . x_j over the
 // multiset of valid entries; all-masked tokens give 0 (lse = -inf).
 //
-// Work decomposition: one workgroup (8 wavefronts) owns one unit = (token t,
-// block of 16 NT heads, NT = 1 or 2) and one split of t's top-k list (at most
-// 2048 entries).  All heads of the block share every gathered row, so Q.X^T
-// is a real [16NT x 512] x [512 x entries] contraction for the matrix cores,
-// and a row is gathered once per block of up to 32 heads.
+// Work decomposition: one workgroup (16 wavefronts, 4 per SIMD) owns one unit
+// = (token t, block of 16 NT heads, NT = 1 or 2) and one split of t's top-k
+// list (at most 2048 entries).  All heads of the block share every gathered
+// row, so Q.X^T is a real [16NT x 512] x [512 x entries] contraction for the
+// matrix cores, and a row is gathered once per block of up to 32 heads.
 //
 //   prologue: the split's indices are resolved once (top-k value -> page
 //     table -> slot; -1 for padding and for invalid values, which are also
-//     counted) into LDS, every phase's loads issued before one wait;
+//     counted) into LDS; the token's page-table row is staged in LDS next to
+//     the top-k loads when it fits;
 //   gather:   rows move HBM -> LDS with global_load_lds_dwordx4 (16 bytes per
-//     lane, no registers), 64-row tiles in 4 LDS buffers, 3 tiles in flight
-//     while one is computed, every wave issuing a share of each tile; the
+//     lane, no registers) in 64-row tiles through 4 LDS buffers.  Every wave
+//     copies the operands it needs from a landed tile into registers at once,
+//     so a buffer is refilled as soon as all waves hold their copy.  The
 //     16-byte chunks of row r are stored XOR-swizzled by (r & 7) so that the
-//     matrix-operand reads below spread over the LDS banks; masked entries
-//     read zero rows;
-//   QK^T:     wave w forms the partial S^T of entries 16(w%4) .. +16 over the
-//     dims half w/4; bf16 query: v_mfma_f32_16x16x32_bf16 on rows converted
-//     FP8 -> bf16 exactly; FP8 query: v_mfma_scale_f32_16x16x128_f8f6f4 on
+//     matrix-operand reads spread over the LDS banks; masked entries read
+//     zero rows;
+//   QK^T:     wave w forms a 16 x 16 partial S^T: entries 16(w%4) .. +16, one
+//     head tile, one part of the 512 dims (NT = 1: four 128-dim quarters;
+//     NT = 2: two 256-dim halves x two head tiles).  bf16 query:
+//     v_mfma_f32_16x16x32_bf16 on rows converted FP8 -> bf16 exactly (exact
+//     products, fp32 sums); FP8 query: v_mfma_scale_f32_16x16x128_f8f6f4 on
 //     the codes themselves (unit block scales), the query scale folded into
-//     the score scale.  The two halves are summed through LDS;
-//   softmax:  the waves agree on the tile max per head through LDS (online
-//     softmax, log2e folded into the scale) and publish P;
-//   PV:       wave w accumulates O^T for dims [64w, 64w+64) over the 64
-//     entries with v_mfma_f32_16x16x32_f16; its A operand (8 entries x 1 dim
-//     per lane) comes straight from the row-major tile through the gfx950
-//     LDS transpose read ds_read_b64_tr_b8 and serves every head tile; P is
-//     rounded to f16.  528-byte rows: group scales multiply the QK partial
-//     sums per 128-wide group and, in PV, multiply P (normalised per tile by
-//     the largest scale, the factor applied to the tile's f32 product);
+//     the score scale;
+//   softmax:  the wave holding part 0 of an entry quarter adds the other
+//     parts (through LDS), keeps its own running maximum per head (log2
+//     domain, moved only when exceeded by more than kSlack, so P <= 2^kSlack)
+//     and denominator, and publishes P (f16) and its maximum;
+//   PV:       wave w accumulates O^T for dims [32w, 32w+32) over the 64
+//     entries with v_mfma_f32_16x16x32_f16, against a per-head reference
+//     maximum M that tracks the largest quarter maximum; P of quarter q is
+//     weighted by 2^(m_q - M) <= 1 on the way into the f16 operand.  The A
+//     operand (8 entries x 1 dim per lane) comes from the row-major tile
+//     through the gfx950 LDS transpose read ds_read_b64_tr_b8.  528-byte
+//     rows: group scales multiply the QK partial sums per 128-wide group and,
+//     in PV, multiply P (normalised per tile by the largest scale, the factor
+//     applied to the tile's f32 product);
+//   schedule: with 16 heads, PV runs one tile behind QK and the next tile's
+//     operands are read from LDS while the owners' softmax and the PV run,
+//     so the LDS traffic (each row is read twice, once per layout) overlaps
+//     the latency-bound phases; two barriers per tile;
 //   epilogue: normalised output + lse, or (several splits) unnormalised
 //     partial (o, m, l) states that a second kernel merges.
 //
@@ -53,6 +65,8 @@
 // of lane l is byte (l & 7) of the 8 bytes addressed by lane 2b + (l >> 3).
 #include <limits.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -63,17 +77,19 @@
 namespace dsa {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 16;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 64;          // entries per tile
-constexpr int kNBuf = 4;           // LDS tile buffers
+constexpr int kNBuf = 4;           // LDS tile buffers (all four in flight)
+constexpr int kNScale = 6;         // scale-word buffers (outlive their tile's rows)
 constexpr int kMaxSplit = 2048;    // entries per workgroup at most
-constexpr int kRowsPerWave = kTile / kWaves;        // DMA share of a tile
+constexpr int kRowsPerWave = kTile / kWaves;        // DMA share of a tile (4 rows)
 constexpr int kLoadsRaw = kRowsPerWave / 2;         // DMA instructions per wave per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kSlack = 8.0f;     // log2 headroom of the running max (P <= 256)
+constexpr float kSlack = 8.0f;     // log2 headroom of a running max (P <= 256)
 // "No maximum yet": finite, so that 2^(-inf - kNoMax) = 0 for masked scores
 // without a select, and far below any real score.
 constexpr float kNoMax = -1.0e30f;
@@ -82,17 +98,32 @@ constexpr float kNoMax = -1.0e30f;
 template <int NT>
 struct Lds {
     static constexpr int kHB = 16 * NT;
+    static constexpr int kParts = 2;                             // QK dim parts
     static constexpr int kBufBytes = kTile * 512;                // 32 KB payload
     static constexpr int kScBytes = kTile * 16;                  // 1 KB scales
     static constexpr int kOffScales = kNBuf * kBufBytes;
-    static constexpr int kOffSlots = kOffScales + kNBuf * kScBytes;
-    static constexpr int kOffP = kOffSlots + kMaxSplit * 4;      // P, aliased with partial S
-    static constexpr int kPBytes = kWaves * kHB * 16 * 4;        // partial S of 8 waves
-    static constexpr int kOffRedM = kOffP + kPBytes;
-    static constexpr int kOffRedL = kOffRedM + kWaves * kHB * 4;
-    static constexpr int kBytes = kOffRedL + kWaves * kHB * 4;
+    static constexpr int kOffSlots = kOffScales + kNScale * kScBytes;
+    // partial S^T of the waves holding dim parts 1.. (16 x 16 fp32 each)
+    static constexpr int kOffSp = kOffSlots + kMaxSplit * 4;
+    static constexpr int kSpBytes = NT * (kParts - 1) * 4 * 1024;
+    // P ([kHB][64] f16, swizzled) and the quarter maxima ([kHB][4] fp32),
+    // two of each (by tile parity)
+    static constexpr int kOffP = kOffSp + kSpBytes;
+    static constexpr int kPBytes = kHB * kTile * 2;
+    static constexpr int kOffMq = kOffP + 2 * kPBytes;
+    static constexpr int kMqBytes = kHB * 16;
+    static constexpr int kOffRedL = kOffMq + 2 * kMqBytes;       // [kHB][4] fp32
+    // 528-byte rows: largest scale of each 128-wide group over a tile, two
+    // tiles (by parity)
+    static constexpr int kOffSmax = kOffRedL + kHB * 16;
+    // per head and quarter: 1 when the quarter's maximum did not move this
+    // tile (then it equals the reference maximum), two tiles (by parity)
+    static constexpr int kOffFlags = kOffSmax + 2 * 16;
+    static constexpr int kBytes = kOffFlags + 2 * kHB * 4;
+    // the token's page-table row is staged over the sp and P areas
+    static constexpr int kPtPer = (kSpBytes + 2 * kPBytes) / 4 / kThreads;
     static_assert(kBytes <= 160 * 1024, "LDS budget");
-    static_assert(kHB * kTile * 4 <= kPBytes, "P fits in the partial-S area");
+    static_assert(kPtPer >= 1, "page-table staging");
 };
 
 // Masked entries read zeros (P = 0 must never meet a NaN of an unreferenced
@@ -120,6 +151,35 @@ __device__ __forceinline__ void wait_lgkm0() {
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
+// Reductions over the four lanes c, c+16, c+32, c+48 (the 16-lane groups g)
+// with the gfx950 cross-half lane swaps (no LDS traffic): v_permlane32_swap
+// exchanges the upper half of its first operand with the lower half of its
+// second, v_permlane16_swap the odd 16-lane rows of the first with the even
+// rows of the second; with both operands equal, the two results hold lanes l
+// and l ^ 32 (resp. l ^ 16).
+// Maximum over all 64 lanes: within each 16-lane row through DPP (quad
+// permutations, then the half-row and row mirrors), then across rows.
+__device__ __forceinline__ float dpp_max16(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));  // quad [1,0,3,2]
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));  // quad [2,3,0,1]
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true))); // half-row mirror
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true))); // row mirror
+    return v;
+}
+
+__device__ __forceinline__ float max_over_g(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_g(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Index resolution of one entry value i, given the page-table word `phys`
 // already fetched for it (see the prologue): -1 -> padding; other invalid
 // values -> masked and counted.
@@ -142,12 +202,14 @@ __device__ __forceinline__ int32_t resolve_entry(const AttnArgs &a, int32_t i,
 
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
-// LDS slot swizzles that keep eight consecutive lanes c of a 16-byte access
-// on distinct banks: the partial-score rows ([head][4 entry groups]) rotate
-// their groups by (c & 7) >> 1, the P rows ([head][16 groups of 4 entries])
-// XOR their group index with c & 7.
+// The partial-score rows ([head][4 entry groups of 4]) rotate their groups by
+// (c & 7) >> 1 so that eight consecutive lanes c of a 16-byte access fall on
+// distinct banks.
 __device__ __forceinline__ int sp_slot(int grp, int c) { return (grp + ((c & 7) >> 1)) & 3; }
-__device__ __forceinline__ int p_slot(int grp, int c) { return grp ^ (c & 7); }
+
+// Byte offset of the 16-byte P chunk k (entries 8k .. 8k+7) of head row hh:
+// rows of 128 bytes, chunks XOR-swizzled by hh & 7.
+__device__ __forceinline__ int p_off(int hh, int k) { return hh * 128 + ((k ^ (hh & 7)) << 4); }
 
 // 32-bit LDS address of a pointer into dynamic shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -167,37 +229,49 @@ __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_base) {
 }
 #pragma clang diagnostic pop
 
-// Issue the DMA of one 64-row tile: wave w moves rows [8w, 8w+8), two rows
-// per instruction (lane l -> row 8w + 2k + (l >> 5), LDS chunk position
-// l & 31, holding global chunk (l & 31) ^ swz(row)); scaled rows add one
-// 8-lane instruction for the rows' 16-byte scale words.
+// Slots of the rows this wave copies for one tile (see issue_tile).
+struct TileSlots {
+    int32_t row[kLoadsRaw];
+    int32_t sc;
+};
+
+template <int LAYOUT>
+__device__ __forceinline__ TileSlots read_slots(const int32_t *slots, int tile_base, int w, int lane) {
+    TileSlots s;
+    const int r0 = kRowsPerWave * w;
+#pragma unroll
+    for (int k = 0; k < kLoadsRaw; k++) s.row[k] = slots[tile_base + r0 + 2 * k + (lane >> 5)];
+    s.sc = LAYOUT == 1 ? slots[tile_base + r0 + (lane & (kRowsPerWave - 1))] : 0;
+    return s;
+}
+
+// Issue the DMA of one 64-row tile into data buffer `buf` and scale buffer
+// `sbuf`: wave w moves rows [4w, 4w+4), two rows per instruction (lane l ->
+// row 4w + 2k + (l >> 5), LDS chunk position l & 31, holding global chunk
+// (l & 31) ^ swz(row)); scaled rows add one 4-lane instruction for the rows'
+// 16-byte scale words.
 template <int LAYOUT, int NT>
-__device__ __forceinline__ void issue_tile(const AttnArgs &a, uint32_t lds0,
-                                           const int32_t *slots, int tile_base,
-                                           int buf, int w, int lane) {
+__device__ __forceinline__ void issue_tile(const AttnArgs &a, uint32_t lds0, const TileSlots &s,
+                                           int buf, int sbuf, int w, int lane) {
     using L = Lds<NT>;
     constexpr int64_t kRow = LAYOUT == 0 ? kRawBytes : kScaledBytes;
     const int r0 = kRowsPerWave * w;
     const uint32_t dst = lds0 + buf * L::kBufBytes + r0 * 512;
     const int pos = lane & 31;
-    int32_t sl[kLoadsRaw];
-#pragma unroll
-    for (int k = 0; k < kLoadsRaw; k++) sl[k] = slots[tile_base + r0 + 2 * k + (lane >> 5)];
 #pragma unroll
     for (int k = 0; k < kLoadsRaw; k++) {
         const int r = r0 + 2 * k + (lane >> 5);
         const int chunk = pos ^ swz(r);
-        const uint8_t *src = sl[k] >= 0 ? a.pool + (int64_t)sl[k] * kRow + chunk * 16
-                                        : kZeroRow + r * kRow + chunk * 16;
+        const uint8_t *src = s.row[k] >= 0 ? a.pool + (int64_t)s.row[k] * kRow + chunk * 16
+                                           : kZeroRow + r * kRow + chunk * 16;
         dma16(src, dst + k * 1024);
     }
     if (LAYOUT == 1) {
         if (lane < kRowsPerWave) {
             const int r = r0 + lane;
-            const int32_t slot = slots[tile_base + r];
-            const uint8_t *src = slot >= 0 ? a.pool + (int64_t)slot * kRow + kD
+            const uint8_t *src = s.sc >= 0 ? a.pool + (int64_t)s.sc * kRow + kD
                                            : kZeroRow + r * kRow + kD;
-            dma16(src, lds0 + L::kOffScales + buf * L::kScBytes + r0 * 16);
+            dma16(src, lds0 + L::kOffScales + sbuf * L::kScBytes + r0 * 16);
         }
     }
 }
@@ -206,13 +280,33 @@ template <int LAYOUT, bool QFP8, bool OUT_BF16, bool SPLIT, int NT>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     using L = Lds<NT>;
     constexpr int kHB = L::kHB;
+    constexpr int kParts = L::kParts;            // dim parts of the QK reduction
+    constexpr int kDP = kD / kParts;             // dims per part: 128 or 256
+    constexpr int kSteps = kDP / 32;             // bf16 K = 32 steps per part
+    constexpr int kSteps8 = kDP / 128;           // FP8 K = 128 steps per part
+    constexpr int kGpp = kDP / 128;              // scale groups per part
+    constexpr int kChunks = kDP / 16;            // 16-byte row chunks per part
+    constexpr int kXc = kDP / 64;                // of which one lane holds (4 lane groups)
+    // Schedule.  Pipelined (16 heads): waves 0-7 score (QK, and the owners'
+    // softmax), waves 8-15 accumulate PV one tile behind, so the owners'
+    // softmax of tile k overlaps the PV of tile k-1 and each tile's operand
+    // reads overlap the phase before.  Sequential (32 heads, whose operands
+    // would not fit the 128 registers a lane has at 16 waves per CU): every
+    // wave scores and accumulates, each tile read, scored, normalised and
+    // accumulated in turn.
+    constexpr bool kPipe = NT == 1;
+    constexpr int kDT = kPipe ? 4 : 2;           // PV: 16-dim tiles per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int kLoads = kLoadsRaw + (LAYOUT == 1 ? 1 : 0);
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
-    const int wq = w & 3;           // QK: entries 16 wq .. +16 of the tile
-    const int hq = w >> 2;          // QK: dims half hq (256 dims)
+    const int wq = w & 3;                        // QK: entries 16 wq .. +16 of the tile
+    const int dp = (w >> 2) % kParts;            // QK: dims part
+    const int ht = (w >> 2) / kParts;            // QK: head tile
+    const bool is_v = kPipe && w >= 8;           // pipelined: a PV-only wave
+    const bool owner = dp == 0 && !is_v;         // adds the parts, forms P
+    const int dbase = kPipe ? 64 * (w - 8) : 32 * w;   // PV: first of this wave's dims
     const int n_hb = (a.H + kHB - 1) / kHB;
 
     // XCD-aware numbering: all of token t's workgroups are 8k + (t % 8)
@@ -225,10 +319,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int split = kq % a.n_splits;
 
     int32_t *slots = reinterpret_cast<int32_t *>(lds + L::kOffSlots);
-    float *p_lds = reinterpret_cast<float *>(lds + L::kOffP);    // [kHB heads][64 entries]
-    float *sp_lds = reinterpret_cast<float *>(lds + L::kOffP);   // [8 waves][kHB heads][16]
-    float *red_m = reinterpret_cast<float *>(lds + L::kOffRedM);
-    float *red_l = reinterpret_cast<float *>(lds + L::kOffRedL);
+    float *sp_lds = reinterpret_cast<float *>(lds + L::kOffSp);     // [waves][16 heads][16]
+    float *rl_lds = reinterpret_cast<float *>(lds + L::kOffRedL);   // [kHB][4 quarters]
 
     const int seq = a.token_seq ? a.token_seq[t] : t;
     const bool seq_ok = (a.page_table == nullptr && a.seq_lens == nullptr) ||
@@ -238,51 +330,45 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int n_ent = min(a.K - begin, a.split_len);   // a multiple of 64
     const int n_tiles = n_ent / kTile;
 
-    // Query of head nt*16 + c as the B operand.  bf16: bq[nt][kk] = q[h][d ..
-    // d+8] with d = (hq*16 + (kk>>1)*4 + g)*16 + (kk&1)*8, so that a lane's
-    // two steps 2m, 2m+1 use one 16-byte chunk of the row; FP8: bq8[nt][k2] =
-    // q8[h][hq*256 + k2*128 + g*32 .. +32].  Heads beyond H read head 0 and
-    // are not stored.
-    bf16x8 bq[QFP8 ? 1 : NT][8];
-    i32x8 bq8[QFP8 ? NT : 1][2];
+    // Query of head ht*16 + c (this wave's QK head tile), dims part dp, as the
+    // B operand.  bf16: bq[kk] = q[h][d .. d+8] with d = (dp*kChunks +
+    // (kk>>1)*4 + g)*16 + (kk&1)*8, so that a lane's steps 2m, 2m+1 use one
+    // 16-byte chunk of the row; FP8: bq8[k2] = q8[h][dp*kDP + k2*128 + g*32 ..
+    // +32].  Heads beyond H read head 0 and are not stored.
+    bf16x8 bq[QFP8 ? 1 : kSteps];
+    i32x8 bq8[QFP8 ? kSteps8 : 1];
     float sscale = a.softmax_scale * kLog2e;
-    if constexpr (QFP8) {
-        sscale *= *a.q_scale;
+    if constexpr (QFP8) sscale *= *a.q_scale;
+    if (!is_v) {
+        const int h = hb * kHB + ht * 16 + c;
+        const int64_t qrow = ((int64_t)t * a.H + (h < a.H ? h : 0)) * kD;
+        if constexpr (QFP8) {
+            const uint8_t *qp = reinterpret_cast<const uint8_t *>(a.q) + qrow + dp * kDP + g * 32;
 #pragma unroll
-        for (int nt = 0; nt < NT; nt++) {
-            const int h = hb * kHB + nt * 16 + c;
-            const uint8_t *qp = reinterpret_cast<const uint8_t *>(a.q) +
-                                ((int64_t)t * a.H + (h < a.H ? h : 0)) * kD + hq * 256 + g * 32;
+            for (int k2 = 0; k2 < kSteps8; k2++)
+                bq8[k2] = *reinterpret_cast<const i32x8 *>(qp + k2 * 128);
+        } else {
+            const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + qrow;
 #pragma unroll
-            for (int k2 = 0; k2 < 2; k2++)
-                bq8[nt][k2] = *reinterpret_cast<const i32x8 *>(qp + k2 * 128);
-        }
-    } else {
-#pragma unroll
-        for (int nt = 0; nt < NT; nt++) {
-            const int h = hb * kHB + nt * 16 + c;
-            const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) +
-                               ((int64_t)t * a.H + (h < a.H ? h : 0)) * kD;
-#pragma unroll
-            for (int kk = 0; kk < 8; kk++)
-                bq[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
-                    qp + (hq * 16 + (kk >> 1) * 4 + g) * 16 + (kk & 1) * 8));
+            for (int kk = 0; kk < kSteps; kk++)
+                bq[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+                    qp + (dp * kChunks + (kk >> 1) * 4 + g) * 16 + (kk & 1) * 8));
         }
     }
 
     // ---- prologue: resolve this split's indices into LDS.  Every load is
     // unconditional (addresses clamped into range, results selected after),
     // so each phase issues all its loads before a single wait.  When the
-    // token's page-table row fits in the (still unused) P area it is staged
-    // there together with the top-k loads, so resolution costs one global
-    // latency instead of two.
+    // token's page-table row fits in the (still unused) sp/P areas it is
+    // staged there together with the top-k loads, so resolution costs one
+    // global latency instead of two.
     {
         constexpr int kPer = kMaxSplit / kThreads;
-        constexpr int kPtCap = L::kPBytes / 4;
-        constexpr int kPtPer = kPtCap / kThreads;
+        constexpr int kPtPer = L::kPtPer;
+        constexpr int kPtCap = kPtPer * kThreads;
         const int32_t *tk = a.topk + (int64_t)t * a.K + begin;
         const int32_t *row = a.page_table + (int64_t)(seq_ok ? seq : 0) * a.max_pages;
-        int32_t *pt_lds = reinterpret_cast<int32_t *>(lds + L::kOffP);
+        int32_t *pt_lds = reinterpret_cast<int32_t *>(lds + L::kOffSp);
         const bool pt_staged = a.page_table != nullptr && a.max_pages <= kPtCap;
         int32_t v[kPer], phys[kPer];
         if (pt_staged) {
@@ -338,363 +424,513 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     __syncthreads();
     const uint32_t lds0 = lds_addr(lds);
 
-    // ---- fill the pipeline
+    // ---- fill the pipeline: one tile per buffer
 #pragma unroll
-    for (int i = 0; i < kNBuf - 1; i++)
-        if (i < n_tiles) issue_tile<LAYOUT, NT>(a, lds0, slots, i * kTile, i, w, lane);
+    for (int i = 0; i < kNBuf; i++)
+        if (i < n_tiles)
+            issue_tile<LAYOUT, NT>(a, lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
+                                   i, w, lane);
 
-    float m_run[NT], l_part[NT];
-    f32x4 acc[4][NT];
+    // Running state.  Owner lanes: the running maximum m_own of head ht*16+c
+    // over their quarter's entries and the lane's share l_part of the
+    // denominator (relative to m_own).  Every wave: the reference maximum
+    // m_ref[nt] of head nt*16+c that O is accumulated against.
+    float m_own = kNoMax, l_part = 0.0f;
+    float m_ref[NT];
+    f32x4 acc[kDT][NT];
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) {
-        m_run[nt] = kNoMax;
-        l_part[nt] = 0.0f;
+        m_ref[nt] = kNoMax;
 #pragma unroll
-        for (int dt = 0; dt < 4; dt++) acc[dt][nt] = f32x4{0, 0, 0, 0};
+        for (int dt = 0; dt < kDT; dt++) acc[dt][nt] = f32x4{0, 0, 0, 0};
     }
+    // Operands of a tile in registers: the QK row chunks (xc) of the tile
+    // being scored, the PV transpose reads (tv) of the last two tiles (by
+    // tile parity; one set when not pipelined).
+    u32x4 xc[kXc];
+    u32x2 tv[kPipe ? 2 : 1][2][kDT];
+    f32x4 part;
 
-    for (int it = 0; it < n_tiles; it++) {
-        const int buf = it % kNBuf;
-        const uint8_t *xb = lds + buf * L::kBufBytes;
-        const f32x4 *scb = reinterpret_cast<const f32x4 *>(lds + L::kOffScales + buf * L::kScBytes);
-        const int32_t *ts = slots + it * kTile;
-
-        // (A) this tile's rows have landed (for this wave), then for all
-        const int ahead = min(kNBuf - 2, n_tiles - 1 - it);
-        if (ahead >= 2) wait_vm_lgkm0<2 * kLoads>();
+    // Wait until this wave's DMA of tile j has landed: `issued` is the last
+    // tile issued so far, later tiles may still be in flight.
+    auto wait_tile = [&](int j, int issued) {
+        const int ahead = min(issued, n_tiles - 1) - j;
+        if (ahead >= 3) wait_vm_lgkm0<3 * kLoads>();
+        else if (ahead == 2) wait_vm_lgkm0<2 * kLoads>();
         else if (ahead == 1) wait_vm_lgkm0<kLoads>();
         else wait_vm_lgkm0<0>();
-        barrier_raw();
-        if (it + kNBuf - 1 < n_tiles)
-            issue_tile<LAYOUT, NT>(a, lds0, slots, (it + kNBuf - 1) * kTile,
-                                   (it + kNBuf - 1) % kNBuf, w, lane);
+    };
 
-        // (B) partial S^T for entries 16 wq .. +16 over dims half hq
-        {
-            const int r = 16 * wq + c;
-            const uint8_t *xr = xb + r * 512;
-            const int sw = swz(r);
-            f32x4 sc4[4];
-            if constexpr (LAYOUT == 1) {
+    // Row chunks of tile j for QK: entry 16 wq + c; bf16 steps 2m, 2m+1 take
+    // the halves of chunk dp*kChunks + 4m + g, FP8 steps k2 the chunk pair
+    // dp*kChunks + 8 k2 + 2g, +1 (a step never leaves a 128-wide scale group).
+    auto read_xc = [&](int j) {
+        const int r = 16 * wq + c;
+        const uint8_t *xr = lds + (j % kNBuf) * L::kBufBytes + r * 512;
+        const int sw = swz(r);
 #pragma unroll
-                for (int i = 0; i < 4; i++) sc4[i] = scb[16 * wq + 4 * g + i];
-            }
-            f32x4 part[NT];
-            if constexpr (QFP8) {
-                // 2 steps of K = 128: dims hq*256 + k2*128 + g*32 .. +32 (two
-                // 16-byte chunks); each step is exactly one scale group
-                u32x4 xa[2][2];
-#pragma unroll
-                for (int k2 = 0; k2 < 2; k2++)
-#pragma unroll
-                    for (int hf = 0; hf < 2; hf++)
-                        xa[k2][hf] = *reinterpret_cast<const u32x4 *>(
-                            xr + (((hq * 16 + k2 * 8 + g * 2 + hf) ^ sw) * 16));
-#pragma unroll
-                for (int nt = 0; nt < NT; nt++) {
-                    f32x4 accg[2];
-#pragma unroll
-                    for (int k2 = 0; k2 < 2; k2++) {
-                        const i32x8 av = {(int)xa[k2][0][0], (int)xa[k2][0][1], (int)xa[k2][0][2],
-                                          (int)xa[k2][0][3], (int)xa[k2][1][0], (int)xa[k2][1][1],
-                                          (int)xa[k2][1][2], (int)xa[k2][1][3]};
-                        accg[k2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            av, bq8[nt][k2], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        if constexpr (LAYOUT == 0)
-                            part[nt][i] = accg[0][i] + accg[1][i];
-                        else
-                            part[nt][i] = accg[0][i] * sc4[i][2 * hq] + accg[1][i] * sc4[i][2 * hq + 1];
-                    }
-                }
-            } else {
-                // 8 steps of K = 32; steps 2m, 2m+1 take the two halves of
-                // chunk hq*16 + 4m + g (so a step's 32 dims stay inside one
-                // 128-wide scale group: group 2hq + m/2)
-                u32x4 xc[4];
-#pragma unroll
-                for (int m = 0; m < 4; m++)
-                    xc[m] = *reinterpret_cast<const u32x4 *>(xr + (((hq * 16 + m * 4 + g) ^ sw) * 16));
-                f32x4 accg[NT][2];
-#pragma unroll
-                for (int nt = 0; nt < NT; nt++) accg[nt][0] = accg[nt][1] = f32x4{0, 0, 0, 0};
-#pragma unroll
-                for (int kk = 0; kk < 8; kk++) {
-                    const u32x4 &ch = xc[kk >> 1];
-                    const bf16x8 av = (kk & 1) ? e4m3x8_to_bf16(ch[2], ch[3])
-                                               : e4m3x8_to_bf16(ch[0], ch[1]);
-                    // raw rows: two independent chains (even / odd kk); scaled
-                    // rows: one chain per 128-wide scale group of this half
-                    const int q = LAYOUT == 0 ? (kk & 1) : (kk >> 2);
-#pragma unroll
-                    for (int nt = 0; nt < NT; nt++)
-                        accg[nt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[nt][kk],
-                                                                              accg[nt][q], 0, 0, 0);
-                }
-#pragma unroll
-                for (int nt = 0; nt < NT; nt++)
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        if constexpr (LAYOUT == 0)
-                            part[nt][i] = accg[nt][0][i] + accg[nt][1][i];
-                        else
-                            part[nt][i] = accg[nt][0][i] * sc4[i][2 * hq] +
-                                          accg[nt][1][i] * sc4[i][2 * hq + 1];
-                    }
-            }
-#pragma unroll
-            for (int nt = 0; nt < NT; nt++)
-                *reinterpret_cast<f32x4 *>(sp_lds + (w * kHB + nt * 16 + c) * 16 +
-                                           4 * sp_slot(g, c)) = part[nt];
+        for (int m = 0; m < kXc; m++) {
+            const int ch = QFP8 ? dp * kChunks + (m >> 1) * 8 + g * 2 + (m & 1)
+                                : dp * kChunks + m * 4 + g;
+            xc[m] = *reinterpret_cast<const u32x4 *>(xr + ((ch ^ sw) * 16));
         }
-        wait_lgkm0();
-        barrier_raw();
+    };
+    // PV operand X^T of tile j via transpose reads: lane (c, g) addresses
+    // entry ks*32 + g*8 + (c >> 1), half (c & 1) of the chunk of dims
+    // dbase + 16dt ..
+    auto read_tv = [&](int j, auto par) {
+        constexpr int PAR = decltype(par)::value;
+        const uint8_t *xb = lds + (j % kNBuf) * L::kBufBytes;
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+            const int row = ks * 32 + g * 8 + (c >> 1);
+            const uint8_t *rp = xb + row * 512 + (c & 1) * 8;
+            const int sw = swz(row);
+#pragma unroll
+            for (int dt = 0; dt < kDT; dt++)
+                tv[PAR][ks][dt] = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_i32x2 *>(
+                               LDS_PTR(rp + (((dbase / 16 + dt) ^ sw) * 16)))));
+        }
+    };
 
-        // (C) full scores of entries 16 wq + 4g + i, heads nt*16 + c; tile max
-        float sv[NT][4];
-        {
-            const int4 sl4 = *reinterpret_cast<const int4 *>(ts + 16 * wq + 4 * g);
-            const int slv[4] = {sl4.x, sl4.y, sl4.z, sl4.w};
+    // Partial S^T of tile j from xc: entries 16 wq .. +16, head tile ht,
+    // dims part dp; published to LDS by the waves holding parts 1..
+    auto qk = [&](int j) {
+        const float *scf = reinterpret_cast<const float *>(lds + L::kOffScales + (j % kNScale) * L::kScBytes);
+        float scv[4][kGpp];
+        if constexpr (LAYOUT == 1) {
 #pragma unroll
-            for (int nt = 0; nt < NT; nt++) {
-                const int hh = nt * 16 + c;
-                const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sp_lds + (wq * kHB + hh) * 16 + 4 * sp_slot(g, c));
-                const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sp_lds + ((wq + 4) * kHB + hh) * 16 + 4 * sp_slot(g, c));
-                float mx = -INFINITY;
+            for (int i = 0; i < 4; i++)
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    sv[nt][i] = slv[i] >= 0 ? (s0[i] + s1[i]) * sscale : -INFINITY;
-                    mx = fmaxf(mx, sv[nt][i]);
+                for (int jj = 0; jj < kGpp; jj++)
+                    scv[i][jj] = scf[(16 * wq + 4 * g + i) * 4 + dp * kGpp + jj];
+        }
+        if constexpr (QFP8) {
+            f32x4 accg[kSteps8];
+#pragma unroll
+            for (int k2 = 0; k2 < kSteps8; k2++) {
+                const u32x4 &lo = xc[2 * k2], &hi = xc[2 * k2 + 1];
+                const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                accg[k2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    av, bq8[k2], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                float s = 0.0f;
+#pragma unroll
+                for (int k2 = 0; k2 < kSteps8; k2++)
+                    s += LAYOUT == 0 ? accg[k2][i] : accg[k2][i] * scv[i][k2];
+                part[i] = s;
+            }
+        } else {
+            f32x4 accg[2];
+            accg[0] = accg[1] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int kk = 0; kk < kSteps; kk++) {
+                const u32x4 &ch = xc[kk >> 1];
+                const bf16x8 av = (kk & 1) ? e4m3x8_to_bf16(ch[2], ch[3])
+                                           : e4m3x8_to_bf16(ch[0], ch[1]);
+                // raw rows: two independent chains (even / odd kk);
+                // scaled rows: one chain per 128-wide scale group
+                const int q = LAYOUT == 0 ? (kk & 1) : (kGpp == 1 ? (kk & 1) : (kk >> 2));
+                accg[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[kk], accg[q], 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                if constexpr (LAYOUT == 0 || kGpp == 1) {
+                    const float s = accg[0][i] + accg[1][i];
+                    part[i] = LAYOUT == 0 ? s : s * scv[i][0];
+                } else {
+                    part[i] = accg[0][i] * scv[i][0] + accg[1][i] * scv[i][kGpp - 1];
                 }
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                if (g == 0 && w < 4) red_m[w * kHB + hh] = mx;
             }
         }
-        wait_lgkm0();
-        barrier_raw();
+        if (!owner) {
+            const int slot = (ht * (kParts - 1) + dp - 1) * 4 + wq;
+            *reinterpret_cast<f32x4 *>(sp_lds + (slot * 16 + c) * 16 + 4 * sp_slot(g, c)) = part;
+        }
+    };
 
-        // (D) shared tile max and probabilities.  The running reference max
-        // only moves when the tile max exceeds it by more than kSlack (log2
-        // units), so the O rescale is rare; P = 2^(s - m_ref) <= 2^kSlack.
-        // All waves see the same maxima and so make the same choice.  Waves
-        // 0-3 own the entries' P and their share of the denominator.
-        {
+    // Owner waves, tile j: full scores of entries 16 wq + 4g + i, head ht*16
+    // + c; running maximum of the quarter (moved only when the tile maximum
+    // exceeds it by more than kSlack, so P <= 2^kSlack); P as f16 into the P
+    // buffer of parity PAR.
+    auto softmax = [&](int j) {
+        const int par = j & 1;
+        float *mq_w = reinterpret_cast<float *>(lds + L::kOffMq + par * L::kMqBytes);
+        uint8_t *p_w = lds + L::kOffP + par * L::kPBytes;
+        const int4 sl4 = *reinterpret_cast<const int4 *>(slots + j * kTile + 16 * wq + 4 * g);
+        const int slv[4] = {sl4.x, sl4.y, sl4.z, sl4.w};
+        f32x4 s = part;
+#pragma unroll
+        for (int pp = 1; pp < kParts; pp++) {
+            const int slot = (ht * (kParts - 1) + pp - 1) * 4 + wq;
+            s += *reinterpret_cast<const f32x4 *>(sp_lds + (slot * 16 + c) * 16 + 4 * sp_slot(g, c));
+        }
+        float sv[4], mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            sv[i] = slv[i] >= 0 ? s[i] * sscale : -INFINITY;
+            mx = fmaxf(mx, sv[i]);
+        }
+        mx = max_over_g(mx);
+        const int hh = ht * 16 + c;
+        if (j > 0) {
+            // adopt the largest quarter maximum of the previous tile, so that
+            // the quarters keep a common reference (their P then needs no
+            // reweighting in PV) until one of them moves
+            const f32x4 mp = *reinterpret_cast<const f32x4 *>(
+                lds + L::kOffMq + (par ^ 1) * L::kMqBytes + hh * 16);
+            const float r = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+            if (r > m_own) {
+                l_part *= __builtin_amdgcn_exp2f(m_own - r);
+                m_own = r;
+            }
+        }
+        const bool moved = mx - m_own > kSlack;   // false for an all-masked tile
+        if (moved) {
+            l_part *= __builtin_amdgcn_exp2f(m_own - mx);
+            m_own = mx;
+        }
+        if (g == 0) lds[L::kOffFlags + par * kHB * 4 + hh * 4 + wq] = j > 0 && !moved;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            p[i] = __builtin_amdgcn_exp2f(sv[i] - m_own);   // masked: 2^-inf = 0
+            l_part += p[i];
+        }
+        const f16x2 p01 = {(_Float16)p[0], (_Float16)p[1]};
+        const f16x2 p23 = {(_Float16)p[2], (_Float16)p[3]};
+        const u32x2 pk = {__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+        *reinterpret_cast<u32x2 *>(p_w + p_off(hh, 2 * wq + (g >> 1)) + (g & 1) * 8) = pk;
+        if (g == 0) mq_w[hh * 4 + wq] = m_own;
+        if constexpr (LAYOUT == 1) {
+            // largest scale of group wq over the tile's 64 entries
+            const float *scf = reinterpret_cast<const float *>(lds + L::kOffScales + (j % kNScale) * L::kScBytes);
+            const float smax = max_over_g(dpp_max16(scf[lane * 4 + wq]));
+            if (lane == 0) reinterpret_cast<float *>(lds + L::kOffSmax)[par * 4 + wq] = smax;
+        }
+    };
+
+    // O^T[dims dbase.., heads] += X^T . P^T over tile j's 64 entries from
+    // tv[TPAR] and the P buffer of parity j & 1; P of quarter q weighted by
+    // 2^(m_q - m_ref) (m_ref = running max of the quarter maxima; O rescaled
+    // when it moves).
+    auto pv = [&](int j, auto tpar) {
+        constexpr int TPAR = decltype(tpar)::value;
+        const int ppar = j & 1;
+        const float *mq_lds = reinterpret_cast<const float *>(lds + L::kOffMq + ppar * L::kMqBytes);
+        const uint8_t *p_lds = lds + L::kOffP + ppar * L::kPBytes;
+        const float *scf = reinterpret_cast<const float *>(lds + L::kOffScales + (j % kNScale) * L::kScBytes);
+        // While every quarter kept the previous reference (all four flags
+        // set) the reference, O and P stay as they are.  Otherwise: m_ref
+        // takes the largest quarter maximum (O rescaled when it moves) and
+        // fq[nt][ks] weights this lane's quarter 2ks + g/2 (read by address:
+        // a register-array select on g would go to scratch).
+        bool uneven = false;
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++)
+            uneven |= *reinterpret_cast<const uint32_t *>(
+                          lds + L::kOffFlags + ppar * kHB * 4 + (nt * 16 + c) * 4) != 0x01010101u;
+        const bool reweight = __ballot(uneven) != 0;
+        float fq[NT][2];
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++) fq[nt][0] = fq[nt][1] = 1.0f;
+        if (reweight) {
             bool any_resc = false;
             float alpha[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; nt++) {
-                const int hh = nt * 16 + c;
-                const float tmax = fmaxf(fmaxf(red_m[hh], red_m[kHB + hh]),
-                                         fmaxf(red_m[2 * kHB + hh], red_m[3 * kHB + hh]));
-                const bool resc = tmax - m_run[nt] > kSlack;   // false for an all-masked tile
-                alpha[nt] = resc ? __builtin_amdgcn_exp2f(m_run[nt] - tmax) : 1.0f;
-                if (resc) m_run[nt] = tmax;
+                const float *mrow = mq_lds + (nt * 16 + c) * 4;
+                const f32x4 mq = *reinterpret_cast<const f32x4 *>(mrow);
+                const float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+                const bool resc = mx > m_ref[nt];
+                alpha[nt] = resc ? __builtin_amdgcn_exp2f(m_ref[nt] - mx) : 1.0f;
+                if (resc) m_ref[nt] = mx;
                 any_resc |= resc;
-                if (w < 4) {
-                    f32x4 p;
-                    float ps = 0.0f;
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        p[i] = __builtin_amdgcn_exp2f(sv[nt][i] - m_run[nt]);   // masked: 2^-inf = 0
-                        ps += p[i];
-                    }
-                    l_part[nt] = l_part[nt] * alpha[nt] + ps;
-                    *reinterpret_cast<f32x4 *>(p_lds + hh * kTile + 4 * p_slot(4 * w + g, c)) = p;
-                }
+                fq[nt][0] = __builtin_amdgcn_exp2f(mrow[g >> 1] - m_ref[nt]);
+                fq[nt][1] = __builtin_amdgcn_exp2f(mrow[2 + (g >> 1)] - m_ref[nt]);
             }
             if (__ballot(any_resc)) {
 #pragma unroll
                 for (int nt = 0; nt < NT; nt++)
 #pragma unroll
-                    for (int dt = 0; dt < 4; dt++) acc[dt][nt] *= alpha[nt];
+                    for (int dt = 0; dt < kDT; dt++) acc[dt][nt] *= alpha[nt];
             }
         }
-        wait_lgkm0();
-        barrier_raw();
-
-        // (E) O^T[dims 64w.., heads] += X^T . P^T over the 64 entries.
-        {
-            // A operand X^T via transpose reads: lane (c, g) addresses entry
-            // e0 + (c >> 1), half (c & 1) of the chunk of dims 64w + 16dt ..
-            u32x2 tv[2][4];
+        // B operand P^T: entries ks*32 + g*8 + r of head nt*16 + c (one
+        // 16-byte chunk, quarter 2ks + g/2)
+        f16x8 bp[NT][2];
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++)
+                bp[nt][ks] = *reinterpret_cast<const f16x8 *>(p_lds + p_off(nt * 16 + c, 4 * ks + g));
+        float smax = 1.0f;
+        if constexpr (LAYOUT == 1) {
+            // scale group dbase/128 of each entry, normalised by the tile's
+            // largest (published with P) so that the f16 operand stays in
+            // range; the factor is put back when the tile's product is added
+            // to O
+            const int grp = dbase >> 7;
+            smax = reinterpret_cast<const float *>(lds + L::kOffSmax)[ppar * 4 + grp];
+            const float inv = smax > 0.0f ? 1.0f / smax : 0.0f;
 #pragma unroll
             for (int ks = 0; ks < 2; ks++) {
-                const int row = ks * 32 + g * 8 + (c >> 1);
-                const uint8_t *rp = xb + row * 512 + (c & 1) * 8;
-                const int sw = swz(row);
+                float sc[8];
 #pragma unroll
-                for (int dt = 0; dt < 4; dt++)
-                    tv[ks][dt] = __builtin_bit_cast(
-                        u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_i32x2 *>(
-                                   LDS_PTR(rp + (((4 * w + dt) ^ sw) * 16)))));
-            }
-            // B operand P^T: entries ks*32 + g*8 + r of head nt*16 + c
-            float pv[NT][2][8];
-#pragma unroll
-            for (int nt = 0; nt < NT; nt++)
-#pragma unroll
-                for (int ks = 0; ks < 2; ks++) {
-                    const float *pp = p_lds + (nt * 16 + c) * kTile;
-                    const f32x4 p0 = *reinterpret_cast<const f32x4 *>(pp + 4 * p_slot(ks * 8 + g * 2, c));
-                    const f32x4 p1 = *reinterpret_cast<const f32x4 *>(pp + 4 * p_slot(ks * 8 + g * 2 + 1, c));
-#pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        pv[nt][ks][r] = p0[r];
-                        pv[nt][ks][4 + r] = p1[r];
-                    }
-                }
-            float smax = 1.0f;
-            if constexpr (LAYOUT == 1) {
-                // scale group w/2 of each entry, normalised by the tile's
-                // largest so that the f16 operand stays in range; the factor
-                // is put back when the tile's product is added to O
-                const float *scf = reinterpret_cast<const float *>(scb);
-                const int grp = w >> 1;
-                float sc[2][8];
-                smax = 0.0f;
-#pragma unroll
-                for (int ks = 0; ks < 2; ks++)
-#pragma unroll
-                    for (int r = 0; r < 8; r++) {
-                        sc[ks][r] = scf[(ks * 32 + g * 8 + r) * 4 + grp];
-                        smax = fmaxf(smax, sc[ks][r]);
-                    }
-                smax = fmaxf(smax, __shfl_xor(smax, 16));
-                smax = fmaxf(smax, __shfl_xor(smax, 32));
-                const float inv = smax > 0.0f ? 1.0f / smax : 0.0f;
-#pragma unroll
-                for (int nt = 0; nt < NT; nt++)
-#pragma unroll
-                    for (int ks = 0; ks < 2; ks++)
-#pragma unroll
-                        for (int r = 0; r < 8; r++) pv[nt][ks][r] *= sc[ks][r] * inv;
-            }
-            f16x8 bp[NT][2];
-#pragma unroll
-            for (int nt = 0; nt < NT; nt++)
-#pragma unroll
-                for (int ks = 0; ks < 2; ks++)
-#pragma unroll
-                    for (int r = 0; r < 8; r++) bp[nt][ks][r] = (_Float16)pv[nt][ks][r];
-#pragma unroll
-            for (int dt = 0; dt < 4; dt++) {
-                const f16x8 av0 = e4m3x8_to_f16(tv[0][dt][0], tv[0][dt][1]);
-                const f16x8 av1 = e4m3x8_to_f16(tv[1][dt][0], tv[1][dt][1]);
+                for (int r = 0; r < 8; r++) sc[r] = scf[(ks * 32 + g * 8 + r) * 4 + grp] * inv;
 #pragma unroll
                 for (int nt = 0; nt < NT; nt++) {
-                    if constexpr (LAYOUT == 0) {
-                        acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, bp[nt][0], acc[dt][nt], 0, 0, 0);
-                        acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bp[nt][1], acc[dt][nt], 0, 0, 0);
+                    f16x8 fac;
+#pragma unroll
+                    for (int r = 0; r < 8; r++) fac[r] = (_Float16)(sc[r] * fq[nt][ks]);
+                    bp[nt][ks] *= fac;
+                }
+            }
+        } else if (reweight) {
+#pragma unroll
+            for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++) bp[nt][ks] *= (_Float16)fq[nt][ks];
+        }
+#pragma unroll
+        for (int dt = 0; dt < kDT; dt++) {
+            const f16x8 av0 = e4m3x8_to_f16(tv[TPAR][0][dt][0], tv[TPAR][0][dt][1]);
+            const f16x8 av1 = e4m3x8_to_f16(tv[TPAR][1][dt][0], tv[TPAR][1][dt][1]);
+#pragma unroll
+            for (int nt = 0; nt < NT; nt++) {
+                if constexpr (LAYOUT == 0) {
+                    acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, bp[nt][0], acc[dt][nt], 0, 0, 0);
+                    acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bp[nt][1], acc[dt][nt], 0, 0, 0);
+                } else {
+                    f32x4 prt = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, bp[nt][0], f32x4{0, 0, 0, 0}, 0, 0, 0);
+                    prt = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bp[nt][1], prt, 0, 0, 0);
+                    acc[dt][nt] += prt * smax;
+                }
+            }
+        }
+    };
+
+    // denominators: the owner lanes' shares, then the four quarters weighted
+    // by 2^(m_q - m_ref); the quarter maxima are the last tile's.  Output or
+    // partial state from the waves that hold O.
+    auto epilogue = [&]() {
+        const float *mq_fin = reinterpret_cast<const float *>(
+            lds + L::kOffMq + ((n_tiles - 1) & 1) * L::kMqBytes);
+        if (owner) {
+            l_part = sum_over_g(l_part);
+            if (g == 0) rl_lds[(ht * 16 + c) * 4 + wq] = l_part;
+        }
+        __syncthreads();
+        if (kPipe && !is_v) return;           // the PV waves hold O
+        const int w_first = kPipe ? 8 : 0;    // writes m, l and lse
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++) {
+            const int hh = nt * 16 + c;
+            const int h = hb * kHB + hh;
+            if (h >= a.H) continue;
+            const f32x4 mq = *reinterpret_cast<const f32x4 *>(mq_fin + hh * 4);
+            const f32x4 lq = *reinterpret_cast<const f32x4 *>(rl_lds + hh * 4);
+            float l_tot = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; q++) l_tot += lq[q] * __builtin_amdgcn_exp2f(mq[q] - m_ref[nt]);
+            const int64_t th = (int64_t)t * a.H + h;
+            if (SPLIT) {
+                float *wo = a.ws + (th * a.n_splits + split) * kD + dbase + 4 * g;
+#pragma unroll
+                for (int dt = 0; dt < kDT; dt++) *reinterpret_cast<f32x4 *>(wo + dt * 16) = acc[dt][nt];
+                if (w == w_first && g == 0) {
+                    float *ml = a.ws + (int64_t)a.T * a.H * a.n_splits * kD +
+                                (th * a.n_splits + split) * 2;
+                    ml[0] = m_ref[nt];
+                    ml[1] = l_tot;
+                }
+            } else {
+                const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+                const int64_t base = th * kD + dbase + 4 * g;
+#pragma unroll
+                for (int dt = 0; dt < kDT; dt++) {
+                    const f32x4 o = acc[dt][nt] * inv;
+                    if (OUT_BF16) {
+                        u32x2 pk = {f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
+                                    f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16)};
+                        *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + base + dt * 16) = pk;
                     } else {
-                        f32x4 prt = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, bp[nt][0], f32x4{0, 0, 0, 0}, 0, 0, 0);
-                        prt = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bp[nt][1], prt, 0, 0, 0);
-                        acc[dt][nt] += prt * smax;
+                        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + base + dt * 16) = o;
                     }
                 }
+                if (a.lse && w == w_first && g == 0)
+                    a.lse[th] = l_tot > 0.0f ? (m_ref[nt] + log2f(l_tot)) * kLn2 : -INFINITY;
             }
         }
-    }
+    };
 
-    // total softmax denominator per head: lanes of this wave, then waves 0-3
-#pragma unroll
-    for (int nt = 0; nt < NT; nt++) {
-        l_part[nt] += __shfl_xor(l_part[nt], 16);
-        l_part[nt] += __shfl_xor(l_part[nt], 32);
-        if (g == 0 && w < 4) red_l[w * kHB + nt * 16 + c] = l_part[nt];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int nt = 0; nt < NT; nt++) {
-        const int hh = nt * 16 + c;
-        const int h = hb * kHB + hh;
-        if (h >= a.H) continue;
-        const float l_tot = red_l[hh] + red_l[kHB + hh] + red_l[2 * kHB + hh] + red_l[3 * kHB + hh];
-        const int64_t th = (int64_t)t * a.H + h;
-        if (SPLIT) {
-            float *wo = a.ws + (th * a.n_splits + split) * kD + 64 * w + 4 * g;
-#pragma unroll
-            for (int dt = 0; dt < 4; dt++) *reinterpret_cast<f32x4 *>(wo + dt * 16) = acc[dt][nt];
-            if (w == 0 && g == 0) {
-                float *ml = a.ws + (int64_t)a.T * a.H * a.n_splits * kD +
-                            (th * a.n_splits + split) * 2;
-                ml[0] = m_run[nt];
-                ml[1] = l_tot;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    if constexpr (kPipe) {
+        // Tile k (parity PAR = k & 1), its operands already in registers:
+        //   scoring waves: QK(k) -> partials;  [tile k+1 landed] barrier;
+        //   scoring waves read tile k+1's row chunks, owners turn tile k's
+        //   scores into P (buffer PAR); PV waves accumulate tile k-1 (P buffer
+        //   PAR^1, tv[PAR^1]) and read tile k+1's transpose operands into
+        //   tv[PAR^1];  barrier;  tile k+1's buffer takes tile k+1+kNBuf.
+        // Both roles pass the same barriers in the same order.
+        auto refill_next = [&](int k, const TileSlots &nsl) {
+            if (k + 1 + kNBuf < n_tiles)
+                issue_tile<LAYOUT, NT>(a, lds0, nsl, (k + 1) % kNBuf, (k + 1 + kNBuf) % kNScale, w, lane);
+        };
+        // tile 0's operands, then its buffer takes tile kNBuf (each role
+        // keeps its own registers: nothing flows from one role's code into
+        // the other's)
+        auto first_tile = [&](auto read_ops) {
+            wait_tile(0, kNBuf - 1);
+            barrier_raw();
+            read_ops();
+            const TileSlots nsl = read_slots<LAYOUT>(slots, min(kNBuf, n_tiles - 1) * kTile, w, lane);
+            wait_lgkm0();
+            barrier_raw();
+            if (kNBuf < n_tiles) issue_tile<LAYOUT, NT>(a, lds0, nsl, 0, kNBuf % kNScale, w, lane);
+        };
+        // (the role test goes through readfirstlane so that the compiler
+        // sees a uniform branch and gives each role its own registers)
+        if (__builtin_amdgcn_readfirstlane((int)is_v)) {
+            first_tile([&] { read_tv(0, I0{}); });
+            auto vstep = [&](int k, auto par) {
+                constexpr int PAR = decltype(par)::value;
+                const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + 1 + kNBuf, n_tiles - 1) * kTile, w, lane);
+                wait_tile(k + 1, k + kNBuf);
+                barrier_raw();
+                if (k > 0) pv(k - 1, std::integral_constant<int, PAR ^ 1>{});
+                if (k + 1 < n_tiles) read_tv(k + 1, std::integral_constant<int, PAR ^ 1>{});
+                wait_lgkm0();
+                barrier_raw();
+                refill_next(k, nsl);
+            };
+            for (int k = 0; k < n_tiles; k += 2) {
+                vstep(k, I0{});
+                if (k + 1 < n_tiles) vstep(k + 1, I1{});
             }
+            if ((n_tiles - 1) & 1) pv(n_tiles - 1, I1{});
+            else pv(n_tiles - 1, I0{});
+            epilogue();
         } else {
-            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-            const int64_t base = th * kD + 64 * w + 4 * g;
-#pragma unroll
-            for (int dt = 0; dt < 4; dt++) {
-                const f32x4 o = acc[dt][nt] * inv;
-                if (OUT_BF16) {
-                    u32x2 pk = {f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
-                                f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16)};
-                    *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + base + dt * 16) = pk;
-                } else {
-                    *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + base + dt * 16) = o;
-                }
+            first_tile([&] { read_xc(0); });
+            for (int k = 0; k < n_tiles; k++) {
+                const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + 1 + kNBuf, n_tiles - 1) * kTile, w, lane);
+                qk(k);
+                wait_tile(k + 1, k + kNBuf);
+                barrier_raw();
+                if (k + 1 < n_tiles) read_xc(k + 1);
+                if (owner) softmax(k);
+                wait_lgkm0();
+                barrier_raw();
+                refill_next(k, nsl);
             }
-            if (a.lse && w == 0 && g == 0)
-                a.lse[th] = l_tot > 0.0f ? (m_run[nt] + log2f(l_tot)) * kLn2 : -INFINITY;
+            epilogue();
         }
+    } else {
+        // P and the quarter maxima alternate between two buffers by tile
+        // parity, so the owners can read the previous tile's maxima while
+        // they publish the current ones
+        for (int k = 0; k < n_tiles; k++) {
+            const bool refill = k + kNBuf < n_tiles;
+            const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + kNBuf, n_tiles - 1) * kTile, w, lane);
+            wait_tile(k, k + kNBuf - 1);
+            barrier_raw();
+            read_xc(k);
+            read_tv(k, I0{});
+            qk(k);
+            // partials published, every wave's operands of this tile are in
+            // registers: the buffer takes the tile kNBuf ahead
+            wait_lgkm0();
+            barrier_raw();
+            if (refill) issue_tile<LAYOUT, NT>(a, lds0, nsl, k % kNBuf, (k + kNBuf) % kNScale, w, lane);
+            if (owner) softmax(k);
+            wait_lgkm0();
+            barrier_raw();
+            pv(k, I0{});
+        }
+        epilogue();
     }
-}
 
+}
 // Merge of the split partial states: one wavefront per (token, head), each
-// lane owning 8 of the 512 dims.
-template <bool OUT_BF16>
+// lane owning 8 of the 512 dims.  Splits are taken CH at a time (CH <= 8,
+// the whole merge for up to eight splits): every (m, l) and o slice of a
+// chunk is loaded before any of them is used, so a chunk costs one memory
+// latency; chunks are merged online.
+template <bool OUT_BF16, int CH>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (th >= (int64_t)a.T * a.H) return;
-    const int S = a.n_splits;
-    const float *ml = a.ws + (int64_t)a.T * a.H * S * kD + th * S * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < S; s++) M = fmaxf(M, ml[2 * s]);
-    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    float Lsum = 0.0f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < S; s++) {
-            const float ms = ml[2 * s];
-            if (ms == -INFINITY) continue;
-            const float wgt = exp2f(ms - M);
-            Lsum += wgt * ml[2 * s + 1];
-            const float *src = a.ws + (th * S + s) * kD + lane * 8;
-            const f32x4 v0 = *reinterpret_cast<const f32x4 *>(src);
-            const f32x4 v1 = *reinterpret_cast<const f32x4 *>(src + 4);
+    const int ns = a.n_splits;
+    const float *ml = a.ws + (int64_t)a.T * a.H * ns * kD + th * ns * 2;
+    const float *ob = a.ws + th * ns * kD + lane * 8;
+    float M = kNoMax, Lsum = 0.0f;
+    f32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
+    for (int s0 = 0; s0 < ns; s0 += CH) {
+        float m[CH], l[CH];
+        f32x4 v0[CH], v1[CH];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                o[i] += wgt * v0[i];
-                o[4 + i] += wgt * v1[i];
-            }
+        for (int k = 0; k < CH; k++) {
+            // splits beyond the last read split 0 and carry no weight
+            const int s = s0 + k < ns ? s0 + k : 0;
+            m[k] = ml[2 * s];
+            l[k] = ml[2 * s + 1];
+            v0[k] = *reinterpret_cast<const f32x4 *>(ob + (int64_t)s * kD);
+            v1[k] = *reinterpret_cast<const f32x4 *>(ob + (int64_t)s * kD + 4);
         }
+        float Mn = M;
+#pragma unroll
+        for (int k = 0; k < CH; k++)
+            if (s0 + k < ns) Mn = fmaxf(Mn, m[k]);
+        // splits with no valid entry carry m = kNoMax, l = 0 and o = 0
+        const float r = __builtin_amdgcn_exp2f(M - Mn);
+        Lsum *= r;
+        o0 *= r;
+        o1 *= r;
+#pragma unroll
+        for (int k = 0; k < CH; k++) {
+            const float wgt = s0 + k < ns ? __builtin_amdgcn_exp2f(m[k] - Mn) : 0.0f;
+            Lsum += wgt * l[k];
+            o0 += wgt * v0[k];
+            o1 += wgt * v1[k];
+        }
+        M = Mn;
     }
     const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+    o0 *= inv;
+    o1 *= inv;
     if (OUT_BF16) {
-        u32x4 pk;
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            pk[i] = f32_to_bf16_bits(o[2 * i] * inv) | (f32_to_bf16_bits(o[2 * i + 1] * inv) << 16);
+        u32x4 pk = {f32_to_bf16_bits(o0[0]) | (f32_to_bf16_bits(o0[1]) << 16),
+                    f32_to_bf16_bits(o0[2]) | (f32_to_bf16_bits(o0[3]) << 16),
+                    f32_to_bf16_bits(o1[0]) | (f32_to_bf16_bits(o1[1]) << 16),
+                    f32_to_bf16_bits(o1[2]) | (f32_to_bf16_bits(o1[3]) << 16)};
         *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(a.out) + th * kD + lane * 8) = pk;
     } else {
         float *dst = reinterpret_cast<float *>(a.out) + th * kD + lane * 8;
-        *reinterpret_cast<f32x4 *>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-        *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+        *reinterpret_cast<f32x4 *>(dst) = o0;
+        *reinterpret_cast<f32x4 *>(dst + 4) = o1;
     }
     if (a.lse && lane == 0) a.lse[th] = Lsum > 0.0f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
 }
 
-// Heads per workgroup: 32 when there are more than 16 heads (a row is then
-// gathered once per 32 heads), else 16.
-static int head_tiles(int H) { return H > 16 ? 2 : 1; }
+// Heads per workgroup: 32 for raw rows when there are more than 16 heads (a
+// row is then gathered once per 32 heads), else 16 (528-byte rows at 32
+// heads would need more than the 128 registers a lane has at 16 waves per
+// CU).
+static int head_tiles(int H, int layout) { return H > 16 && layout == 0 ? 2 : 1; }
+
+constexpr int kMaxSplits = 32;     // K <= 65536 with 2048 entries per split
 
 // Splits per (token, head block): enough workgroups to cover the CUs for
 // small batches, and never more than kMaxSplit entries per workgroup.
-int attn_decode_splits(int T, int H, int K) {
-    const int hbw = 16 * head_tiles(H);
+int attn_decode_splits(int T, int H, int K, int layout) {
+    const int hbw = 16 * head_tiles(H, layout);
     const int64_t units = (int64_t)T * ((H + hbw - 1) / hbw);
     const int tiles = K / kTile;
     if (units <= 0 || tiles <= 0) return 1;
@@ -702,6 +938,7 @@ int attn_decode_splits(int T, int H, int K) {
     const int64_t s_min = (K + kMaxSplit - 1) / kMaxSplit;
     if (s < s_min) s = s_min;
     if (s > tiles) s = tiles;
+    if (s > kMaxSplits) s = kMaxSplits;
     const int tps = (int)((tiles + s - 1) / s);
     return (tiles + tps - 1) / tps;
 }
@@ -713,23 +950,39 @@ static int split_len_for(int K, int splits) {
     return ((tiles + splits - 1) / splits) * kTile;
 }
 
-int attn_splits(int T, int H, int K, int phase) {
-    return phase == 0 ? attn_decode_splits(T, H, K) : prefill_splits(K);
+int attn_splits(int T, int H, int K, int phase, int layout) {
+    return phase == 0 ? attn_decode_splits(T, H, K, layout) : prefill_splits(K);
 }
 
+// Layout 0 has the fewest head blocks and so the most splits: its size
+// covers every layout.
 size_t attn_workspace_bytes(int T, int H, int K, int phase) {
-    const int s = attn_splits(T, H, K, phase);
+    const int s = attn_splits(T, H, K, phase, 0);
     if (s <= 1) return 0;
     size_t b = (size_t)T * H * s * (kD + 2) * sizeof(float);
     return (b + 255) & ~(size_t)255;
 }
 
-template <typename Kern>
-static void allow_big_lds(Kern kern, int bytes) {
-    // once per instantiation; not a stream operation, so capture-safe
+// Dynamic LDS above the default limit, set once per kernel instantiation (a
+// function attribute, not a stream operation, so graph capture is unaffected).
+template <auto Kern>
+static void allow_big_lds(int bytes) {
     static const hipError_t e = hipFuncSetAttribute(
-        (const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        (const void *)Kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     (void)e;
+}
+
+template <bool OUT_BF16, int CH>
+static void launch_combine(const AttnArgs &a, hipStream_t stream) {
+    const dim3 cgrid((unsigned)(((int64_t)a.T * a.H + 3) / 4));
+    attn_combine_kernel<OUT_BF16, CH><<<cgrid, dim3(256), 0, stream>>>(a);
+}
+
+template <bool OUT_BF16>
+static void launch_combine_s(const AttnArgs &a, hipStream_t stream) {
+    if (a.n_splits <= 2) return launch_combine<OUT_BF16, 2>(a, stream);
+    if (a.n_splits <= 4) return launch_combine<OUT_BF16, 4>(a, stream);
+    return launch_combine<OUT_BF16, 8>(a, stream);
 }
 
 template <int LAYOUT, bool QFP8, bool OUT_BF16, int NT>
@@ -739,14 +992,13 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)(((int64_t)a.T + 7) / 8 * 8 * n_hb * a.n_splits));
     constexpr int bytes = Lds<NT>::kBytes;
     if (a.n_splits > 1) {
-        auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, true, NT>;
-        allow_big_lds(kern, bytes);
+        constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, true, NT>;
+        allow_big_lds<kern>(bytes);
         kern<<<grid, dim3(kThreads), bytes, stream>>>(a);
-        const dim3 cgrid((unsigned)(((int64_t)a.T * a.H + 3) / 4));
-        attn_combine_kernel<OUT_BF16><<<cgrid, dim3(256), 0, stream>>>(a);
+        launch_combine_s<OUT_BF16>(a, stream);
     } else {
-        auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, false, NT>;
-        allow_big_lds(kern, bytes);
+        constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, false, NT>;
+        allow_big_lds<kern>(bytes);
         kern<<<grid, dim3(kThreads), bytes, stream>>>(a);
     }
     return hipGetLastError();
@@ -754,8 +1006,10 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
 
 template <int LAYOUT, bool QFP8, bool OUT_BF16>
 static hipError_t launch_nt(const AttnArgs &a, hipStream_t stream) {
-    return head_tiles(a.H) == 2 ? launch_one<LAYOUT, QFP8, OUT_BF16, 2>(a, stream)
-                                : launch_one<LAYOUT, QFP8, OUT_BF16, 1>(a, stream);
+    if constexpr (LAYOUT == 0) {
+        if (head_tiles(a.H, LAYOUT) == 2) return launch_one<LAYOUT, QFP8, OUT_BF16, 2>(a, stream);
+    }
+    return launch_one<LAYOUT, QFP8, OUT_BF16, 1>(a, stream);
 }
 
 hipError_t launch_attn(const AttnArgs &a_in, int layout, bool q_fp8, bool out_bf16,

@@ -41,8 +41,8 @@ struct AttnArgs {
 };
 
 // Number of top-k splits for this shape and phase (1 = none).
-int attn_decode_splits(int T, int H, int K);
-int attn_splits(int T, int H, int K, int phase);
+int attn_decode_splits(int T, int H, int K, int layout);
+int attn_splits(int T, int H, int K, int phase, int layout);
 size_t attn_workspace_bytes(int T, int H, int K, int phase);
 
 hipError_t launch_attn(const AttnArgs &a, int layout, bool q_fp8, bool out_bf16,
