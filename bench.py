@@ -166,15 +166,16 @@ def main():
     attn_avg_s = float(np.mean(attn_ms)) * 1e-3
     tok_s = T * args.steps / elapsed
 
+    traffic = committed_traffic(wl.name)
     if prefill:
         achieved = flops / attn_avg_s / 1e12
         roofline = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_TFLOPS,
-                    "traffic": None}
+                    "traffic": traffic}
     else:
         achieved = gathered / attn_avg_s / 1e9
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None}
+                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic}
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -218,6 +219,32 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
+def committed_traffic(workload):
+    """HBM bytes of one attention call as measured by the rocprofv3 counter
+    runs summarised in profiles/attn_<workload>_traffic.txt (FETCH_SIZE and
+    WRITE_SIZE per dispatch, scaled by what the same counters read for a 1 GiB
+    device copy), or None when there is no such summary or the kernel source
+    has changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attn_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        k, v = line.split()[:2]
+        fields[k] = v
+    h = hashlib.sha256()
+    for f in ("sparse_mla_attention_gather_amd/csrc/attn.hip",
+              "sparse_mla_attention_gather_amd/csrc/common.h"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    return float(fields["traffic_bytes_per_call"])
+
+
 def cpu_baseline(wl, budget_s):
     """The oracle (as it stands) on a bounded sample of the same workload:
     whole steps (writer on the new rows + attention for every token of the
@@ -228,6 +255,7 @@ def cpu_baseline(wl, budget_s):
 
     orc = oracle.get()
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cores = max(1, min(cores, 16))      # the host-core share of one GPU
     R = wl.row_bytes
     rng = np.random.default_rng(wl.seed + 1000)
     T_s = wl.T
@@ -256,7 +284,7 @@ def cpu_baseline(wl, budget_s):
         t_total += time.perf_counter() - t0
         steps += 1
         tokens += T_s
-        if t_total >= budget_s or steps >= 50:
+        if t_total >= budget_s or steps >= 500:
             break
     return {"value": tokens / t_total, "unit": "tok/s", "cores": cores,
             "kind": "oracle",

@@ -296,6 +296,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // accumulated in turn.
     constexpr bool kPipe = NT == 1;
     constexpr int kDT = kPipe ? 4 : 2;           // PV: 16-dim tiles per wave
+#ifndef DSA_FILL0
+#define DSA_FILL0 2
+#endif
+    constexpr int kFill0 = DSA_FILL0;            // tiles requested before the first lands
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int kLoads = kLoadsRaw + (LAYOUT == 1 ? 1 : 0);
     const int tid = threadIdx.x, lane = tid & 63;
@@ -424,12 +428,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     __syncthreads();
     const uint32_t lds0 = lds_addr(lds);
 
-    // ---- fill the pipeline: one tile per buffer
+    // ---- fill the pipeline: the first kFill0 tiles now, the other buffers
+    // once tile 0 has landed (requested all at once, every workgroup's first
+    // tile would come back only with the rest of the burst)
 #pragma unroll
-    for (int i = 0; i < kNBuf; i++)
+    for (int i = 0; i < kFill0; i++)
         if (i < n_tiles)
             issue_tile<LAYOUT, NT>(a, lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
                                    i, w, lane);
+    auto fill_rest = [&]() {
+#pragma unroll
+        for (int i = kFill0; i < kNBuf; i++)
+            if (i < n_tiles)
+                issue_tile<LAYOUT, NT>(a, lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
+                                       i, w, lane);
+    };
 
     // Running state.  Owner lanes: the running maximum m_own of head ht*16+c
     // over their quarter's entries and the lane's share l_part of the
@@ -786,8 +799,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         // keeps its own registers: nothing flows from one role's code into
         // the other's)
         auto first_tile = [&](auto read_ops) {
-            wait_tile(0, kNBuf - 1);
+            wait_tile(0, kFill0 - 1);
             barrier_raw();
+            fill_rest();
             read_ops();
             const TileSlots nsl = read_slots<LAYOUT>(slots, min(kNBuf, n_tiles - 1) * kTile, w, lane);
             wait_lgkm0();
@@ -838,8 +852,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         for (int k = 0; k < n_tiles; k++) {
             const bool refill = k + kNBuf < n_tiles;
             const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + kNBuf, n_tiles - 1) * kTile, w, lane);
-            wait_tile(k, k + kNBuf - 1);
+            wait_tile(k, k == 0 ? kFill0 - 1 : k + kNBuf - 1);
             barrier_raw();
+            if (k == 0) fill_rest();
             read_xc(k);
             read_tv(k, I0{});
             qk(k);
