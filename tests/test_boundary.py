@@ -231,3 +231,20 @@ def test_quantize_rejections():
     assert f(**{**q, "n_elems": 0, "q": None}) == dsa.DSA_OK
     assert dsa.dsa_quantize_q_workspace_bytes(0) == 0
     assert dsa.dsa_quantize_q_workspace_bytes(8) == 4
+
+
+# ------------------------------------------------------------------ build check
+
+def test_build_rejects_kernels_that_use_scratch():
+    """The build refuses kernels with spills or scratch: the attention kernel
+    counts outstanding vector-memory operations to wait for its tile copies."""
+    from sparse_mla_attention_gather_amd import build as B
+    ok = ("x.hip:1:1: remark: Function Name: k_ok [-Rpass-analysis=kernel-resource-usage]\n"
+          "x.hip:1:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]\n"
+          "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]\n")
+    bad = ("x.hip:9:1: remark: Function Name: k_bad [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:9:1: remark:     VGPRs Spill: 3 [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 16 [-Rpass-analysis=kernel-resource-usage]\n")
+    assert B.scratch_users(ok) == []
+    assert B.scratch_users(ok + bad) == [("k_bad", "VGPRs Spill", 3),
+                                         ("k_bad", "ScratchSize [bytes/lane]", 16)]
