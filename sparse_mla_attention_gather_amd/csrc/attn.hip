@@ -570,18 +570,28 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // + c; running maximum of the quarter (moved only when the tile maximum
     // exceeds it by more than kSlack, so P <= 2^kSlack); P as f16 into the P
     // buffer of parity PAR.
-    auto softmax = [&](int j) {
+    // `then` runs after the softmax's own LDS reads are issued (the
+    // pipelined schedule issues the next tile's operand reads there, so that
+    // they queue behind the softmax's and not in front of them).
+    auto softmax = [&](int j, auto then) {
         const int par = j & 1;
         float *mq_w = reinterpret_cast<float *>(lds + L::kOffMq + par * L::kMqBytes);
         uint8_t *p_w = lds + L::kOffP + par * L::kPBytes;
+        const int hh = ht * 16 + c;
         const int4 sl4 = *reinterpret_cast<const int4 *>(slots + j * kTile + 16 * wq + 4 * g);
-        const int slv[4] = {sl4.x, sl4.y, sl4.z, sl4.w};
         f32x4 s = part;
 #pragma unroll
         for (int pp = 1; pp < kParts; pp++) {
             const int slot = (ht * (kParts - 1) + pp - 1) * 4 + wq;
             s += *reinterpret_cast<const f32x4 *>(sp_lds + (slot * 16 + c) * 16 + 4 * sp_slot(g, c));
         }
+        const f32x4 mp = *reinterpret_cast<const f32x4 *>(
+            lds + L::kOffMq + (par ^ 1) * L::kMqBytes + hh * 16);
+        float sc_own = 0.0f;
+        if constexpr (LAYOUT == 1)
+            sc_own = reinterpret_cast<const float *>(lds + L::kOffScales + (j % kNScale) * L::kScBytes)[lane * 4 + wq];
+        then();
+        const int slv[4] = {sl4.x, sl4.y, sl4.z, sl4.w};
         float sv[4], mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -589,13 +599,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             mx = fmaxf(mx, sv[i]);
         }
         mx = max_over_g(mx);
-        const int hh = ht * 16 + c;
         if (j > 0) {
             // adopt the largest quarter maximum of the previous tile, so that
             // the quarters keep a common reference (their P then needs no
             // reweighting in PV) until one of them moves
-            const f32x4 mp = *reinterpret_cast<const f32x4 *>(
-                lds + L::kOffMq + (par ^ 1) * L::kMqBytes + hh * 16);
             const float r = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
             if (r > m_own) {
                 l_part *= __builtin_amdgcn_exp2f(m_own - r);
@@ -621,18 +628,24 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         if (g == 0) mq_w[hh * 4 + wq] = m_own;
         if constexpr (LAYOUT == 1) {
             // largest scale of group wq over the tile's 64 entries
-            const float *scf = reinterpret_cast<const float *>(lds + L::kOffScales + (j % kNScale) * L::kScBytes);
-            const float smax = max_over_g(dpp_max16(scf[lane * 4 + wq]));
+            const float smax = max_over_g(dpp_max16(sc_own));
             if (lane == 0) reinterpret_cast<float *>(lds + L::kOffSmax)[par * 4 + wq] = smax;
         }
     };
+    auto nothing = [] {};
 
     // O^T[dims dbase.., heads] += X^T . P^T over tile j's 64 entries from
     // tv[TPAR] and the P buffer of parity j & 1; P of quarter q weighted by
     // 2^(m_q - m_ref) (m_ref = running max of the quarter maxima; O rescaled
     // when it moves).
-    auto pv = [&](int j, auto tpar) {
-        constexpr int TPAR = decltype(tpar)::value;
+    // PV in two steps: pv_prep(j) fixes the reference maximum, rescales O
+    // and loads tile j's P operand (pv_bp, with the weights applied);
+    // pv_mma(TPAR, DT0, DT1) then accumulates dim tiles [DT0, DT1) from
+    // tv[TPAR].  The pipelined schedule splits the dim tiles over its two
+    // phases.
+    f16x8 pv_bp[NT][2];
+    float pv_smax = 1.0f;
+    auto pv_prep = [&](int j) {
         const int ppar = j & 1;
         const float *mq_lds = reinterpret_cast<const float *>(lds + L::kOffMq + ppar * L::kMqBytes);
         const uint8_t *p_lds = lds + L::kOffP + ppar * L::kPBytes;
@@ -642,6 +655,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         // takes the largest quarter maximum (O rescaled when it moves) and
         // fq[nt][ks] weights this lane's quarter 2ks + g/2 (read by address:
         // a register-array select on g would go to scratch).
+        // B operand P^T: entries ks*32 + g*8 + r of head nt*16 + c (one
+        // 16-byte chunk, quarter 2ks + g/2); read together with the flags
+        auto &bp = pv_bp;
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++)
+                bp[nt][ks] = *reinterpret_cast<const f16x8 *>(p_lds + p_off(nt * 16 + c, 4 * ks + g));
         bool uneven = false;
 #pragma unroll
         for (int nt = 0; nt < NT; nt++)
@@ -673,14 +694,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                     for (int dt = 0; dt < kDT; dt++) acc[dt][nt] *= alpha[nt];
             }
         }
-        // B operand P^T: entries ks*32 + g*8 + r of head nt*16 + c (one
-        // 16-byte chunk, quarter 2ks + g/2)
-        f16x8 bp[NT][2];
-#pragma unroll
-        for (int nt = 0; nt < NT; nt++)
-#pragma unroll
-            for (int ks = 0; ks < 2; ks++)
-                bp[nt][ks] = *reinterpret_cast<const f16x8 *>(p_lds + p_off(nt * 16 + c, 4 * ks + g));
         float smax = 1.0f;
         if constexpr (LAYOUT == 1) {
             // scale group dbase/128 of each entry, normalised by the tile's
@@ -709,22 +722,33 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ks++) bp[nt][ks] *= (_Float16)fq[nt][ks];
         }
+        pv_smax = smax;
+    };
+    auto pv_mma = [&](auto tpar, auto dt0, auto dt1) {
+        constexpr int TPAR = decltype(tpar)::value;
 #pragma unroll
-        for (int dt = 0; dt < kDT; dt++) {
+        for (int dt = decltype(dt0)::value; dt < decltype(dt1)::value; dt++) {
             const f16x8 av0 = e4m3x8_to_f16(tv[TPAR][0][dt][0], tv[TPAR][0][dt][1]);
             const f16x8 av1 = e4m3x8_to_f16(tv[TPAR][1][dt][0], tv[TPAR][1][dt][1]);
 #pragma unroll
             for (int nt = 0; nt < NT; nt++) {
                 if constexpr (LAYOUT == 0) {
-                    acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, bp[nt][0], acc[dt][nt], 0, 0, 0);
-                    acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bp[nt][1], acc[dt][nt], 0, 0, 0);
+                    acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, pv_bp[nt][0], acc[dt][nt], 0, 0, 0);
+                    acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, pv_bp[nt][1], acc[dt][nt], 0, 0, 0);
                 } else {
-                    f32x4 prt = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, bp[nt][0], f32x4{0, 0, 0, 0}, 0, 0, 0);
-                    prt = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bp[nt][1], prt, 0, 0, 0);
-                    acc[dt][nt] += prt * smax;
+                    f32x4 prt = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, pv_bp[nt][0], f32x4{0, 0, 0, 0}, 0, 0, 0);
+                    prt = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, pv_bp[nt][1], prt, 0, 0, 0);
+                    acc[dt][nt] += prt * pv_smax;
                 }
             }
         }
+    };
+    using DT0 = std::integral_constant<int, 0>;
+    using DTH = std::integral_constant<int, kDT / 2>;
+    using DTN = std::integral_constant<int, kDT>;
+    auto pv = [&](int j, auto tpar) {
+        pv_prep(j);
+        pv_mma(tpar, DT0{}, DTN{});
     };
 
     // denominators: the owner lanes' shares, then the four quarters weighted
@@ -752,9 +776,23 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             for (int q = 0; q < 4; q++) l_tot += lq[q] * __builtin_amdgcn_exp2f(mq[q] - m_ref[nt]);
             const int64_t th = (int64_t)t * a.H + h;
             if (SPLIT) {
-                float *wo = a.ws + (th * a.n_splits + split) * kD + dbase + 4 * g;
+                // the split's normalised output o / l (raw rows: f16, whose
+                // range holds any average of E4M3 values; 528-byte rows:
+                // fp32), then (m, l)
+                const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+                const int64_t po = (th * a.n_splits + split) * kD + dbase + 4 * g;
 #pragma unroll
-                for (int dt = 0; dt < kDT; dt++) *reinterpret_cast<f32x4 *>(wo + dt * 16) = acc[dt][nt];
+                for (int dt = 0; dt < kDT; dt++) {
+                    const f32x4 o = acc[dt][nt] * inv;
+                    if constexpr (LAYOUT == 0) {
+                        const f16x2 o01 = {(_Float16)o[0], (_Float16)o[1]};
+                        const f16x2 o23 = {(_Float16)o[2], (_Float16)o[3]};
+                        *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.ws) + po + dt * 16) =
+                            u32x2{__builtin_bit_cast(uint32_t, o01), __builtin_bit_cast(uint32_t, o23)};
+                    } else {
+                        *reinterpret_cast<f32x4 *>(a.ws + po + dt * 16) = o;
+                    }
+                }
                 if (w == w_first && g == 0) {
                     float *ml = a.ws + (int64_t)a.T * a.H * a.n_splits * kD +
                                 (th * a.n_splits + split) * 2;
@@ -785,11 +823,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     using I1 = std::integral_constant<int, 1>;
     if constexpr (kPipe) {
         // Tile k (parity PAR = k & 1), its operands already in registers:
-        //   scoring waves: QK(k) -> partials;  [tile k+1 landed] barrier;
-        //   scoring waves read tile k+1's row chunks, owners turn tile k's
-        //   scores into P (buffer PAR); PV waves accumulate tile k-1 (P buffer
-        //   PAR^1, tv[PAR^1]) and read tile k+1's transpose operands into
-        //   tv[PAR^1];  barrier;  tile k+1's buffer takes tile k+1+kNBuf.
+        //   scoring waves: QK(k) -> partials; PV waves: the first half of
+        //   tile k-1's dims (P buffer PAR^1, tv[PAR^1]);  [tile k+1 landed]
+        //   barrier;  scoring waves read tile k+1's row chunks, owners turn
+        //   tile k's scores into P (buffer PAR); PV waves: the other half,
+        //   then read tile k+1's transpose operands into tv[PAR^1];  barrier;
+        //   tile k+1's buffer takes tile k+1+kNBuf.
         // Both roles pass the same barriers in the same order.
         auto refill_next = [&](int k, const TileSlots &nsl) {
             if (k + 1 + kNBuf < n_tiles)
@@ -815,10 +854,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             auto vstep = [&](int k, auto par) {
                 constexpr int PAR = decltype(par)::value;
                 const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + 1 + kNBuf, n_tiles - 1) * kTile, w, lane);
+                using TP = std::integral_constant<int, PAR ^ 1>;
+                if (k > 0) {
+                    pv_prep(k - 1);
+                    pv_mma(TP{}, DT0{}, DTH{});
+                }
                 wait_tile(k + 1, k + kNBuf);
                 barrier_raw();
-                if (k > 0) pv(k - 1, std::integral_constant<int, PAR ^ 1>{});
-                if (k + 1 < n_tiles) read_tv(k + 1, std::integral_constant<int, PAR ^ 1>{});
+                if (k > 0) pv_mma(TP{}, DTH{}, DTN{});
+                if (k + 1 < n_tiles) read_tv(k + 1, TP{});
                 wait_lgkm0();
                 barrier_raw();
                 refill_next(k, nsl);
@@ -837,8 +881,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 qk(k);
                 wait_tile(k + 1, k + kNBuf);
                 barrier_raw();
-                if (k + 1 < n_tiles) read_xc(k + 1);
-                if (owner) softmax(k);
+                if (owner) softmax(k, [&] { if (k + 1 < n_tiles) read_xc(k + 1); });
+                else if (k + 1 < n_tiles) read_xc(k + 1);
                 wait_lgkm0();
                 barrier_raw();
                 refill_next(k, nsl);
@@ -863,7 +907,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             wait_lgkm0();
             barrier_raw();
             if (refill) issue_tile<LAYOUT, NT>(a, lds0, nsl, k % kNBuf, (k + kNBuf) % kNScale, w, lane);
-            if (owner) softmax(k);
+            if (owner) softmax(k, nothing);
             wait_lgkm0();
             barrier_raw();
             pv(k, I0{});
@@ -873,18 +917,20 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 
 }
 // Merge of the split partial states: one wavefront per (token, head), each
-// lane owning 8 of the 512 dims.  Splits are taken CH at a time (CH <= 8,
-// the whole merge for up to eight splits): every (m, l) and o slice of a
-// chunk is loaded before any of them is used, so a chunk costs one memory
-// latency; chunks are merged online.
-template <bool OUT_BF16, int CH>
+// lane owning 8 of the 512 dims.  A split holds its normalised output o_s
+// (f16 for raw rows, fp32 for 528-byte rows) and (m_s, l_s); the merge is
+// sum_s 2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s.  Splits are taken CH at
+// a time (CH <= 8, the whole merge for up to eight splits): every split's
+// state in a chunk is loaded before any of it is used, so a chunk costs one
+// memory latency; chunks are merged online.
+template <bool OUT_BF16, int CH, bool F16>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (th >= (int64_t)a.T * a.H) return;
     const int ns = a.n_splits;
     const float *ml = a.ws + (int64_t)a.T * a.H * ns * kD + th * ns * 2;
-    const float *ob = a.ws + th * ns * kD + lane * 8;
+    const int64_t ob = th * ns * kD + lane * 8;
     float M = kNoMax, Lsum = 0.0f;
     f32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
     for (int s0 = 0; s0 < ns; s0 += CH) {
@@ -896,8 +942,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
             const int s = s0 + k < ns ? s0 + k : 0;
             m[k] = ml[2 * s];
             l[k] = ml[2 * s + 1];
-            v0[k] = *reinterpret_cast<const f32x4 *>(ob + (int64_t)s * kD);
-            v1[k] = *reinterpret_cast<const f32x4 *>(ob + (int64_t)s * kD + 4);
+            if constexpr (F16) {
+                const f16x8 h = *reinterpret_cast<const f16x8 *>(
+                    reinterpret_cast<const _Float16 *>(a.ws) + ob + (int64_t)s * kD);
+                v0[k] = __builtin_convertvector(h.lo, f32x4);
+                v1[k] = __builtin_convertvector(h.hi, f32x4);
+            } else {
+                v0[k] = *reinterpret_cast<const f32x4 *>(a.ws + ob + (int64_t)s * kD);
+                v1[k] = *reinterpret_cast<const f32x4 *>(a.ws + ob + (int64_t)s * kD + 4);
+            }
         }
         float Mn = M;
 #pragma unroll
@@ -910,8 +963,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
         o1 *= r;
 #pragma unroll
         for (int k = 0; k < CH; k++) {
-            const float wgt = s0 + k < ns ? __builtin_amdgcn_exp2f(m[k] - Mn) : 0.0f;
-            Lsum += wgt * l[k];
+            const float wgt = s0 + k < ns ? __builtin_amdgcn_exp2f(m[k] - Mn) * l[k] : 0.0f;
+            Lsum += wgt;
             o0 += wgt * v0[k];
             o1 += wgt * v1[k];
         }
@@ -987,17 +1040,17 @@ static void allow_big_lds(int bytes) {
     (void)e;
 }
 
-template <bool OUT_BF16, int CH>
+template <bool OUT_BF16, int CH, bool F16>
 static void launch_combine(const AttnArgs &a, hipStream_t stream) {
     const dim3 cgrid((unsigned)(((int64_t)a.T * a.H + 3) / 4));
-    attn_combine_kernel<OUT_BF16, CH><<<cgrid, dim3(256), 0, stream>>>(a);
+    attn_combine_kernel<OUT_BF16, CH, F16><<<cgrid, dim3(256), 0, stream>>>(a);
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool F16>
 static void launch_combine_s(const AttnArgs &a, hipStream_t stream) {
-    if (a.n_splits <= 2) return launch_combine<OUT_BF16, 2>(a, stream);
-    if (a.n_splits <= 4) return launch_combine<OUT_BF16, 4>(a, stream);
-    return launch_combine<OUT_BF16, 8>(a, stream);
+    if (a.n_splits <= 2) return launch_combine<OUT_BF16, 2, F16>(a, stream);
+    if (a.n_splits <= 4) return launch_combine<OUT_BF16, 4, F16>(a, stream);
+    return launch_combine<OUT_BF16, 8, F16>(a, stream);
 }
 
 template <int LAYOUT, bool QFP8, bool OUT_BF16, int NT>
@@ -1010,7 +1063,7 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
         constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, true, NT>;
         allow_big_lds<kern>(bytes);
         kern<<<grid, dim3(kThreads), bytes, stream>>>(a);
-        launch_combine_s<OUT_BF16>(a, stream);
+        launch_combine_s<OUT_BF16, LAYOUT == 0>(a, stream);
     } else {
         constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, false, NT>;
         allow_big_lds<kern>(bytes);

@@ -146,6 +146,12 @@ SMALL = [
     dict(seed=207, T=7, H=5, K=128, layout=W.RAW, page_size=1),
     dict(seed=208, T=2, H=16, K=2048, layout=W.SCALED, seq_len=3000, page_size=64,
          dup_frac=0.1, neg_frac=0.05),
+    # enough tokens that decode splits the list into several multi-tile
+    # pieces (more tiles per piece than tile buffers, a shorter last piece)
+    dict(seed=209, T=48, H=16, K=1664, layout=W.RAW, seq_len=2500, page_size=64),
+    dict(seed=210, T=40, H=32, K=1664, layout=W.SCALED, seq_len=2000, page_size=64,
+         neg_frac=0.05),
+    dict(seed=211, T=24, H=64, K=896, layout=W.RAW, seq_len=1200, page_size=32),
 ]
 
 
