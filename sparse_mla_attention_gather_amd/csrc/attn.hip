@@ -332,7 +332,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int seq_len = (a.seq_lens && seq_ok) ? a.seq_lens[seq] : INT_MAX;
     const int begin = split * a.split_len;
     const int n_ent = min(a.K - begin, a.split_len);   // a multiple of 64
-    const int n_tiles = n_ent / kTile;
 
     // Query of head ht*16 + c (this wave's QK head tile), dims part dp, as the
     // B operand.  bf16: bq[kk] = q[h][d .. d+8] with d = (dp*kChunks +
@@ -408,7 +407,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 for (int i = 0; i < kPer; i++) phys[i] = 0;
             }
         }
-        int n_err = 0;
+        // last valid entry of each wave (ballot of the resolved slots; j
+        // grows with the lane): the tiles after the split's last valid entry
+        // hold only masked entries, which contribute nothing, and are skipped
+        int n_err = 0, last = -1;
 #pragma unroll
         for (int i = 0; i < kPer; i++) {
             const int j = tid + i * kThreads;
@@ -416,7 +418,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             const int32_t s = resolve_entry(a, v[i], phys[i], seq_ok, seq_len, err);
             n_err += err;
             if (j < n_ent) slots[j] = s;
+            const uint64_t vb = __builtin_amdgcn_ballot_w64(j < n_ent && s >= 0);
+            if (vb) last = max(last, w * 64 + 63 - (int)__builtin_clzll(vb) + i * kThreads);
         }
+        if (lane == 0) reinterpret_cast<int *>(rl_lds)[w] = last;
         if (a.err_count && hb == 0) {
 #pragma unroll
             for (int s = 1; s < 64; s <<= 1) n_err += __shfl_xor(n_err, s);
@@ -427,6 +432,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // the loop the only outstanding vector-memory operations are tile DMAs
     __syncthreads();
     const uint32_t lds0 = lds_addr(lds);
+    // tiles up to the one holding the last valid entry (at least one: an
+    // all-masked split still runs one tile and leaves l = 0)
+    int n_tiles;
+    {
+        const int4 *lw = reinterpret_cast<const int4 *>(rl_lds);
+        int last = -1;
+#pragma unroll
+        for (int i = 0; i < kWaves / 4; i++) {
+            const int4 v4 = lw[i];
+            last = max(max(last, max(v4.x, v4.y)), max(v4.z, v4.w));
+        }
+        n_tiles = __builtin_amdgcn_readfirstlane(max(1, (last + kTile) / kTile));
+    }
 
     // ---- fill the pipeline: the first kFill0 tiles now, the other buffers
     // once tile 0 has landed (requested all at once, every workgroup's first

@@ -183,6 +183,34 @@ def test_attention_small(orc, cfg, phase, qfp8, od):
         assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
 
 
+@pytest.mark.parametrize("H", [16, 32])
+@pytest.mark.parametrize("layout", [W.RAW, W.SCALED], ids=["raw", "scaled"])
+@pytest.mark.parametrize("phase", [0, 1], ids=["decode", "prefill"])
+def test_trailing_masked_entries(orc, layout, phase, H):
+    """Rows whose valid entries end early (every later entry -1, as ragged
+    widths padded to the row width): widths 0, 1, 63, 64, 65, mid-list and
+    full, across several multi-tile splits.  The tiles after a split's last
+    valid entry are skipped, which must not change any result."""
+    widths = [0, 1, 63, 64, 65, 700, 1023, 1024, 1500, 1664]
+    T = 6 * len(widths)
+    wl = W.small(301 + layout, T=T, H=H, K=1664, layout=layout, seq_len=2500,
+                 page_size=64, neg_frac=0.0)
+    topk = wl.topk.copy()
+    for t in range(T):
+        topk[t, widths[t % len(widths)]:] = -1
+    wl = W.Workload(**{**wl.__dict__, "topk": topk})
+    pool = P.build_pool(orc, wl)
+    di = G.DevInputs(wl)
+    ref, ref_lse, ref_err = _oracle_attn(orc, wl, pool)
+    out, lse, err = G.run_attn(di, G.dev(pool), phase=phase)
+    assert err == ref_err == 0
+    G.assert_attn_close(out, ref, where=f"trailing -1, layout {layout}, phase {phase}")
+    G.assert_lse_close(lse, ref_lse)
+    for t in range(T):
+        if widths[t % len(widths)] == 0:
+            assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
+
+
 def test_invalid_indices_are_masked_and_counted(orc):
     wl = W.small(301, T=4, H=16, K=256, neg_frac=0.25, seq_len=120)
     bad = wl.topk.copy()
