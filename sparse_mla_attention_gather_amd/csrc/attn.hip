@@ -287,14 +287,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     constexpr int kGpp = kDP / 128;              // scale groups per part
     constexpr int kChunks = kDP / 16;            // 16-byte row chunks per part
     constexpr int kXc = kDP / 64;                // of which one lane holds (4 lane groups)
-    // Schedule.  Pipelined (16 heads): waves 0-7 score (QK, and the owners'
-    // softmax), waves 8-15 accumulate PV one tile behind, so the owners'
-    // softmax of tile k overlaps the PV of tile k-1 and each tile's operand
-    // reads overlap the phase before.  Sequential (32 heads, whose operands
-    // would not fit the 128 registers a lane has at 16 waves per CU): every
-    // wave scores and accumulates, each tile read, scored, normalised and
-    // accumulated in turn.
-    constexpr bool kPipe = NT == 1;
+    // Schedule.  Pipelined (16 heads; 32 heads with FP8 queries): waves 0-7
+    // score (QK over every head tile, and the owners' softmax), waves 8-15
+    // accumulate PV one tile behind, so the owners' softmax of tile k
+    // overlaps the PV of tile k-1 and each tile's operand reads overlap the
+    // phase before.  Sequential (32 heads with bf16 queries, whose 64
+    // registers of query per scoring lane would not fit the 128 a lane has
+    // at 16 waves per CU): every wave scores and accumulates, each tile
+    // read, scored, normalised and accumulated in turn.
+    constexpr bool kPipe = NT == 1 || QFP8;
+    static_assert(kParts == 2, "one publishing wave per head tile and quarter");
+    constexpr bool kLate = kPipe && NT == 2;     // PV operands read in their own step
     constexpr int kDT = kPipe ? 4 : 2;           // PV: 16-dim tiles per wave
 #ifndef DSA_FILL0
 #define DSA_FILL0 2
@@ -307,9 +310,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int c = lane & 15, g = lane >> 4;
     const int wq = w & 3;                        // QK: entries 16 wq .. +16 of the tile
     const int dp = (w >> 2) % kParts;            // QK: dims part
-    const int ht = (w >> 2) / kParts;            // QK: head tile
     const bool is_v = kPipe && w >= 8;           // pipelined: a PV-only wave
-    const bool owner = dp == 0 && !is_v;         // adds the parts, forms P
+    // Scoring.  Pipelined: a scoring wave computes dims part dp of every head
+    // tile; head tile ht is owned (parts added, P formed) by the waves with
+    // dp == ht, and the other part's wave publishes its partial.  16 heads:
+    // the dp = 1 waves only publish.  Sequential: wave w scores head tile
+    // (w >> 2) / kParts only, and the dp = 0 waves own it.
+    const int ht = kPipe ? (NT == 1 ? 0 : dp) : (w >> 2) / kParts;
+    const bool owner = !is_v && (kPipe ? (NT == 1 ? dp == 0 : true) : dp == 0);
+    constexpr int kQT = kPipe ? NT : 1;          // head tiles a scoring wave scores
     const int dbase = kPipe ? 64 * (w - 8) : 32 * w;   // PV: first of this wave's dims
     const int n_hb = (a.H + kHB - 1) / kHB;
 
@@ -333,29 +342,32 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int begin = split * a.split_len;
     const int n_ent = min(a.K - begin, a.split_len);   // a multiple of 64
 
-    // Query of head ht*16 + c (this wave's QK head tile), dims part dp, as the
-    // B operand.  bf16: bq[kk] = q[h][d .. d+8] with d = (dp*kChunks +
-    // (kk>>1)*4 + g)*16 + (kk&1)*8, so that a lane's steps 2m, 2m+1 use one
-    // 16-byte chunk of the row; FP8: bq8[k2] = q8[h][dp*kDP + k2*128 + g*32 ..
-    // +32].  Heads beyond H read head 0 and are not stored.
-    bf16x8 bq[QFP8 ? 1 : kSteps];
-    i32x8 bq8[QFP8 ? kSteps8 : 1];
+    // Query of head (ht or nt)*16 + c of each scored head tile, dims part dp,
+    // as the B operand.  bf16: bq[nt][kk] = q[h][d .. d+8] with d = (dp*kChunks
+    // + (kk>>1)*4 + g)*16 + (kk&1)*8, so that a lane's steps 2m, 2m+1 use one
+    // 16-byte chunk of the row; FP8: bq8[nt][k2] = q8[h][dp*kDP + k2*128 +
+    // g*32 .. +32].  Heads beyond H read head 0 and are not stored.
+    bf16x8 bq[QFP8 ? 1 : kQT][QFP8 ? 1 : kSteps];
+    i32x8 bq8[QFP8 ? kQT : 1][QFP8 ? kSteps8 : 1];
     float sscale = a.softmax_scale * kLog2e;
     if constexpr (QFP8) sscale *= *a.q_scale;
     if (!is_v) {
-        const int h = hb * kHB + ht * 16 + c;
-        const int64_t qrow = ((int64_t)t * a.H + (h < a.H ? h : 0)) * kD;
-        if constexpr (QFP8) {
-            const uint8_t *qp = reinterpret_cast<const uint8_t *>(a.q) + qrow + dp * kDP + g * 32;
 #pragma unroll
-            for (int k2 = 0; k2 < kSteps8; k2++)
-                bq8[k2] = *reinterpret_cast<const i32x8 *>(qp + k2 * 128);
-        } else {
-            const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + qrow;
+        for (int nt = 0; nt < kQT; nt++) {
+            const int h = hb * kHB + (kPipe ? nt : ht) * 16 + c;
+            const int64_t qrow = ((int64_t)t * a.H + (h < a.H ? h : 0)) * kD;
+            if constexpr (QFP8) {
+                const uint8_t *qp = reinterpret_cast<const uint8_t *>(a.q) + qrow + dp * kDP + g * 32;
 #pragma unroll
-            for (int kk = 0; kk < kSteps; kk++)
-                bq[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
-                    qp + (dp * kChunks + (kk >> 1) * 4 + g) * 16 + (kk & 1) * 8));
+                for (int k2 = 0; k2 < kSteps8; k2++)
+                    bq8[nt][k2] = *reinterpret_cast<const i32x8 *>(qp + k2 * 128);
+            } else {
+                const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + qrow;
+#pragma unroll
+                for (int kk = 0; kk < kSteps; kk++)
+                    bq[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+                        qp + (dp * kChunks + (kk >> 1) * 4 + g) * 16 + (kk & 1) * 8));
+            }
         }
     }
 
@@ -477,10 +489,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     }
     // Operands of a tile in registers: the QK row chunks (xc) of the tile
     // being scored, the PV transpose reads (tv) of the last two tiles (by
-    // tile parity; one set when not pipelined).
+    // tile parity; one set when not pipelined or with kLate).
     u32x4 xc[kXc];
-    u32x2 tv[kPipe ? 2 : 1][2][kDT];
-    f32x4 part;
+    u32x2 tv[kPipe && !kLate ? 2 : 1][2][kDT];
+    f32x4 part[kQT];
 
     // Wait until this wave's DMA of tile j has landed: `issued` is the last
     // tile issued so far, later tiles may still be in flight.
@@ -525,8 +537,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         }
     };
 
-    // Partial S^T of tile j from xc: entries 16 wq .. +16, head tile ht,
-    // dims part dp; published to LDS by the waves holding parts 1..
+    // Partial S^T of tile j from xc: entries 16 wq .. +16, dims part dp, of
+    // each scored head tile (part[nt]; each converted operand feeds every
+    // head tile).  The partial of a head tile the wave does not own goes to
+    // LDS slot (head tile)*4 + wq, for its owner.
     auto qk = [&](int j) {
         const float *scf = reinterpret_cast<const float *>(lds + L::kOffScales + (j % kNScale) * L::kScBytes);
         float scv[4][kGpp];
@@ -538,49 +552,64 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                     scv[i][jj] = scf[(16 * wq + 4 * g + i) * 4 + dp * kGpp + jj];
         }
         if constexpr (QFP8) {
-            f32x4 accg[kSteps8];
 #pragma unroll
-            for (int k2 = 0; k2 < kSteps8; k2++) {
-                const u32x4 &lo = xc[2 * k2], &hi = xc[2 * k2 + 1];
-                const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                accg[k2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    av, bq8[k2], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
-            }
+            for (int nt = 0; nt < kQT; nt++) {
+                f32x4 accg[kSteps8];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                float s = 0.0f;
+                for (int k2 = 0; k2 < kSteps8; k2++) {
+                    const u32x4 &lo = xc[2 * k2], &hi = xc[2 * k2 + 1];
+                    const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    accg[k2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        av, bq8[nt][k2], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
+                }
 #pragma unroll
-                for (int k2 = 0; k2 < kSteps8; k2++)
-                    s += LAYOUT == 0 ? accg[k2][i] : accg[k2][i] * scv[i][k2];
-                part[i] = s;
+                for (int i = 0; i < 4; i++) {
+                    float s = 0.0f;
+#pragma unroll
+                    for (int k2 = 0; k2 < kSteps8; k2++)
+                        s += LAYOUT == 0 ? accg[k2][i] : accg[k2][i] * scv[i][k2];
+                    part[nt][i] = s;
+                }
             }
         } else {
-            f32x4 accg[2];
-            accg[0] = accg[1] = f32x4{0, 0, 0, 0};
+            // raw rows: two independent chains (even / odd kk) for one head
+            // tile, one per head tile for two; scaled rows (one head tile):
+            // one chain per 128-wide scale group
+            constexpr int kCh = (LAYOUT == 0 && kQT > 1) ? 1 : 2;
+            f32x4 accg[kQT][2];
+#pragma unroll
+            for (int nt = 0; nt < kQT; nt++) accg[nt][0] = accg[nt][1] = f32x4{0, 0, 0, 0};
 #pragma unroll
             for (int kk = 0; kk < kSteps; kk++) {
                 const u32x4 &ch = xc[kk >> 1];
                 const bf16x8 av = (kk & 1) ? e4m3x8_to_bf16(ch[2], ch[3])
                                            : e4m3x8_to_bf16(ch[0], ch[1]);
-                // raw rows: two independent chains (even / odd kk);
-                // scaled rows: one chain per 128-wide scale group
-                const int q = LAYOUT == 0 ? (kk & 1) : (kGpp == 1 ? (kk & 1) : (kk >> 2));
-                accg[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[kk], accg[q], 0, 0, 0);
+                const int q = LAYOUT == 0 ? (kCh == 2 ? (kk & 1) : 0)
+                                          : (kGpp == 1 ? (kk & 1) : (kk >> 2));
+#pragma unroll
+                for (int nt = 0; nt < kQT; nt++)
+                    accg[nt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[nt][kk], accg[nt][q], 0, 0, 0);
             }
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                if constexpr (LAYOUT == 0 || kGpp == 1) {
-                    const float s = accg[0][i] + accg[1][i];
-                    part[i] = LAYOUT == 0 ? s : s * scv[i][0];
-                } else {
-                    part[i] = accg[0][i] * scv[i][0] + accg[1][i] * scv[i][kGpp - 1];
+            for (int nt = 0; nt < kQT; nt++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    if constexpr (LAYOUT == 0 || kGpp == 1) {
+                        const float s = kCh == 2 ? accg[nt][0][i] + accg[nt][1][i] : accg[nt][0][i];
+                        part[nt][i] = LAYOUT == 0 ? s : s * scv[i][0];
+                    } else {
+                        part[nt][i] = accg[nt][0][i] * scv[i][0] + accg[nt][1][i] * scv[i][kGpp - 1];
+                    }
                 }
-            }
         }
-        if (!owner) {
-            const int slot = (ht * (kParts - 1) + dp - 1) * 4 + wq;
-            *reinterpret_cast<f32x4 *>(sp_lds + (slot * 16 + c) * 16 + 4 * sp_slot(g, c)) = part;
+#pragma unroll
+        for (int nt = 0; nt < kQT; nt++) {
+            const int qt = kPipe ? nt : ht;          // head tile of part[nt]
+            if (!(owner && qt == ht)) {
+                const int slot = qt * 4 + wq;
+                *reinterpret_cast<f32x4 *>(sp_lds + (slot * 16 + c) * 16 + 4 * sp_slot(g, c)) = part[nt];
+            }
         }
     };
 
@@ -597,10 +626,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         uint8_t *p_w = lds + L::kOffP + par * L::kPBytes;
         const int hh = ht * 16 + c;
         const int4 sl4 = *reinterpret_cast<const int4 *>(slots + j * kTile + 16 * wq + 4 * g);
-        f32x4 s = part;
-#pragma unroll
-        for (int pp = 1; pp < kParts; pp++) {
-            const int slot = (ht * (kParts - 1) + pp - 1) * 4 + wq;
+        // own part of the owned head tile plus the other part's, published
+        f32x4 s = (kQT == 1 || ht == 0) ? part[0] : part[kQT - 1];
+        {
+            const int slot = ht * 4 + wq;
             s += *reinterpret_cast<const f32x4 *>(sp_lds + (slot * 16 + c) * 16 + 4 * sp_slot(g, c));
         }
         const f32x4 mp = *reinterpret_cast<const f32x4 *>(
@@ -848,13 +877,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         //   then read tile k+1's transpose operands into tv[PAR^1];  barrier;
         //   tile k+1's buffer takes tile k+1+kNBuf.
         // Both roles pass the same barriers in the same order.
-        auto refill_next = [&](int k, const TileSlots &nsl) {
-            if (k + 1 + kNBuf < n_tiles)
-                issue_tile<LAYOUT, NT>(a, lds0, nsl, (k + 1) % kNBuf, (k + 1 + kNBuf) % kNScale, w, lane);
+        // 32 heads (kLate): the PV waves read tile k's transpose operands in
+        // step k itself, into a single register set, and tile k's buffer
+        // (not tile k+1's) takes the next tile after step k, so that kNBuf - 1
+        // tiles rather than kNBuf are in flight beyond the one being scored.
+        constexpr int kAhead = kLate ? kNBuf - 1 : kNBuf;
+        auto refill = [&](int k, const TileSlots &nsl) {
+            const int nx = k + 1 + kAhead;
+            if (nx < n_tiles)
+                issue_tile<LAYOUT, NT>(a, lds0, nsl, nx % kNBuf, nx % kNScale, w, lane);
         };
-        // tile 0's operands, then its buffer takes tile kNBuf (each role
-        // keeps its own registers: nothing flows from one role's code into
-        // the other's)
+        // tile 0's operands, then (16 heads) its buffer takes tile kNBuf
+        // (each role keeps its own registers: nothing flows from one role's
+        // code into the other's)
         auto first_tile = [&](auto read_ops) {
             wait_tile(0, kFill0 - 1);
             barrier_raw();
@@ -863,47 +898,50 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             const TileSlots nsl = read_slots<LAYOUT>(slots, min(kNBuf, n_tiles - 1) * kTile, w, lane);
             wait_lgkm0();
             barrier_raw();
-            if (kNBuf < n_tiles) issue_tile<LAYOUT, NT>(a, lds0, nsl, 0, kNBuf % kNScale, w, lane);
+            if (!kLate && kNBuf < n_tiles) issue_tile<LAYOUT, NT>(a, lds0, nsl, 0, kNBuf % kNScale, w, lane);
         };
         // (the role test goes through readfirstlane so that the compiler
         // sees a uniform branch and gives each role its own registers)
         if (__builtin_amdgcn_readfirstlane((int)is_v)) {
-            first_tile([&] { read_tv(0, I0{}); });
+            first_tile([&] { if constexpr (!kLate) read_tv(0, I0{}); });
             auto vstep = [&](int k, auto par) {
                 constexpr int PAR = decltype(par)::value;
-                const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + 1 + kNBuf, n_tiles - 1) * kTile, w, lane);
-                using TP = std::integral_constant<int, PAR ^ 1>;
+                const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + 1 + kAhead, n_tiles - 1) * kTile, w, lane);
+                // tv set of tiles k-1 and k+1 (kLate: the one set, tiles
+                // k-1 then k)
+                using TP = std::integral_constant<int, kLate ? 0 : PAR ^ 1>;
                 if (k > 0) {
                     pv_prep(k - 1);
                     pv_mma(TP{}, DT0{}, DTH{});
                 }
-                wait_tile(k + 1, k + kNBuf);
+                wait_tile(k + 1, k + kAhead);
                 barrier_raw();
                 if (k > 0) pv_mma(TP{}, DTH{}, DTN{});
-                if (k + 1 < n_tiles) read_tv(k + 1, TP{});
+                if constexpr (kLate) read_tv(k, TP{});
+                else if (k + 1 < n_tiles) read_tv(k + 1, TP{});
                 wait_lgkm0();
                 barrier_raw();
-                refill_next(k, nsl);
+                refill(k, nsl);
             };
             for (int k = 0; k < n_tiles; k += 2) {
                 vstep(k, I0{});
                 if (k + 1 < n_tiles) vstep(k + 1, I1{});
             }
-            if ((n_tiles - 1) & 1) pv(n_tiles - 1, I1{});
+            if (!kLate && ((n_tiles - 1) & 1)) pv(n_tiles - 1, I1{});
             else pv(n_tiles - 1, I0{});
             epilogue();
         } else {
             first_tile([&] { read_xc(0); });
             for (int k = 0; k < n_tiles; k++) {
-                const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + 1 + kNBuf, n_tiles - 1) * kTile, w, lane);
+                const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + 1 + kAhead, n_tiles - 1) * kTile, w, lane);
                 qk(k);
-                wait_tile(k + 1, k + kNBuf);
+                wait_tile(k + 1, k + kAhead);
                 barrier_raw();
                 if (owner) softmax(k, [&] { if (k + 1 < n_tiles) read_xc(k + 1); });
                 else if (k + 1 < n_tiles) read_xc(k + 1);
                 wait_lgkm0();
                 barrier_raw();
-                refill_next(k, nsl);
+                refill(k, nsl);
             }
             epilogue();
         }
