@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (counter scaling)")
+    ap.add_argument("--op", default="attention", choices=["attention", "transform"],
+                    help="transform: time the index transform alone on the "
+                         "workload's top-k rows (page table -> compacted slots)")
     return ap.parse_args()
 
 
@@ -71,6 +74,8 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     wl = W.NAMED[args.workload]()
+    if args.op == "transform":
+        return bench_transform(args, wl, dev)
     T, H, K, R = wl.T, wl.H, wl.K, wl.row_bytes
     prefill = wl.q_fp8
     phase = 1 if prefill else 0
@@ -225,14 +230,85 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def committed_traffic(workload):
-    """HBM bytes of one attention call as measured by the rocprofv3 counter
-    runs summarised in profiles/attn_<workload>_traffic.txt (FETCH_SIZE and
+def bench_transform(args, wl, dev):
+    """The index transform alone: each step resolves and compacts every
+    top-k row of the workload (same rows each step).  Algorithmic bytes per
+    call: the int32 top-k read, the int32 slots and counts written; the
+    page-table words are read once per entry but come from cache."""
+    import torch
+
+    import sparse_mla_attention_gather_amd as dsa
+
+    T, K = wl.topk.shape
+    d = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    topk, pt, ts, sl = d(wl.topk), d(wl.page_table), d(wl.token_seq), d(wl.seq_lens)
+    num_seqs, max_pages = (0, 0) if wl.page_table is None else wl.page_table.shape
+    out = torch.empty((T, K), dtype=torch.int32, device=dev)
+    counts = torch.empty(T, dtype=torch.int32, device=dev)
+
+    def call():
+        dsa.check(dsa.dsa_topk_transform(topk, T, K, pt, wl.page_size, max_pages, num_seqs,
+                                         ts, sl, wl.num_slots, out, K, counts, None))
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    sampled = set(range(0, args.steps, EV_EVERY))
+    events = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for i in sampled}
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev = events.get(i)
+        if ev:
+            ev[0].record()
+        call()
+        if ev:
+            ev[1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    call_s = float(np.mean([a.elapsed_time(b) for a, b in events.values()])) * 1e-3
+    nbytes = 4 * T * K + 4 * T * K + 4 * T
+    achieved = nbytes / call_s / 1e9
+    rec = {
+        "metric": "top-k entries/s, index transform (page table -> compacted slots)",
+        "value": T * K * args.steps / elapsed,
+        "unit": "entries/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32", "data": "synthetic",
+        "config": {"workload": f"topk_transform/{wl.name}", "T": T, "k_in": K, "k_out": K,
+                   "page_size": wl.page_size},
+        "transform_us": call_s * 1e6,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": committed_traffic(wl.name, "topk_transform",
+                                                  "topk_transform.hip")},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        import oracle
+        orc = oracle.get()
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            orc.topk_transform(wl.topk, wl.num_slots, K, page_table=wl.page_table,
+                               page_size=wl.page_size, token_seq=wl.token_seq,
+                               seq_lens=wl.seq_lens)
+            n += 1
+        rec["cpu_baseline"] = {"value": T * K * n / (time.perf_counter() - t0),
+                               "unit": "entries/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} whole transform(s) of the {wl.name} rows"}
+    print(json.dumps(rec), flush=True)
+
+
+def committed_traffic(workload, op="attn", source="attn.hip"):
+    """HBM bytes of one call as measured by the rocprofv3 counter runs
+    summarised in profiles/<op>_<workload>_traffic.txt (FETCH_SIZE and
     WRITE_SIZE per dispatch, scaled by what the same counters read for a 1 GiB
     device copy), or None when there is no such summary or the kernel source
     has changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"attn_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{op}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -242,7 +318,7 @@ def committed_traffic(workload):
         k, v = line.split()[:2]
         fields[k] = v
     h = hashlib.sha256()
-    for f in ("sparse_mla_attention_gather_amd/csrc/attn.hip",
+    for f in (f"sparse_mla_attention_gather_amd/csrc/{source}",
               "sparse_mla_attention_gather_amd/csrc/common.h"):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())

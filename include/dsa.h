@@ -203,6 +203,39 @@ int32_t dsa_sparse_attn_prefill(
  * (0 = decode, 1 = prefill); a pure function of its arguments. */
 size_t dsa_attn_workspace_bytes(int32_t T, int32_t H, int32_t K, int32_t phase);
 
+/*
+ * dsa_topk_transform -- the index transform ahead of the attention: top-k
+ * positions of any width resolved to physical pool slots and compacted
+ * ["[DSA] Support group-scaled FP8 NoPE KV reads for CUDA TileLang", the
+ * draft notes: the page-table transform over non-2048 top-k widths; Q8,
+ * review thread: prefix requests read only the referenced context slots
+ * through the flattened page table (the RAGGED path)].
+ *
+ * Every entry of row t is resolved with exactly the attention's rule (see
+ * dsa_sparse_attn_decode: -1 is padding; the same invalid values are masked
+ * and counted into *err_count).  Row t of out_slots then holds the valid
+ * slots in their input order, followed by -1 up to k_out, and valid_count[t]
+ * their number.  out_slots is what the attention takes with page_table ==
+ * NULL (its width k_out already a multiple of 128), and the attention skips
+ * the tiles after a row's last valid entry.
+ *
+ *   topk        [T, k_in] int32, 1 <= k_in <= 65536 (any width).
+ *   page_table, page_size, max_pages, num_seqs, token_seq, seq_lens,
+ *   num_slots   as for the attention.
+ *   out_slots   [T, k_out] int32, fully overwritten; k_out a multiple of 128
+ *               with k_in <= k_out <= 65536; must not overlap topk.
+ *   valid_count [T] int32 or NULL.
+ *   err_count   one int32 (device) that masked entries are added to, or NULL.
+ *   T == 0 is a no-op.  Asynchronous on `stream` (NULL = the default stream);
+ *   argument errors are returned before anything is launched.
+ */
+int32_t dsa_topk_transform(const int32_t *topk, int32_t T, int32_t k_in,
+                           const int32_t *page_table, int32_t page_size,
+                           int32_t max_pages, int32_t num_seqs,
+                           const int32_t *token_seq, const int32_t *seq_lens,
+                           int64_t num_slots, int32_t *out_slots, int32_t k_out,
+                           int32_t *valid_count, int32_t *err_count, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

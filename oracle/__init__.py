@@ -49,7 +49,8 @@ class Oracle:
     """ctypes view of one compiled oracle library."""
 
     def __init__(self, path: str = LIB):
-        if not os.path.exists(path):
+        if not os.path.exists(path) or (
+                path == LIB and os.path.getmtime(path) < os.path.getmtime(SRC)):
             build(out=path)
         self.path = path
         lib = ctypes.CDLL(path)
@@ -72,6 +73,10 @@ class Oracle:
         lib.orc_resolve.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p,
                                     c_int, c_int, c_void_p, c_int64, c_void_p]
         lib.orc_sparse_attn.restype = c_int64
+        lib.orc_topk_transform.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p,
+                                           c_int, c_int, c_void_p, c_int64, c_int,
+                                           c_void_p, c_void_p]
+        lib.orc_topk_transform.restype = c_int64
         lib.orc_sparse_attn.argtypes = [
             c_void_p, c_int, c_float, c_int, c_int, c_void_p, c_int64, c_int,
             c_void_p, c_int, c_void_p, c_int, c_int, c_void_p, c_void_p,
@@ -130,6 +135,23 @@ class Oracle:
                                    _ptr(_c(seq_lens, np.int32)), num_slots,
                                    _ptr(slots))
         return slots, int(err)
+
+    def topk_transform(self, topk, num_slots, k_out, page_table=None, page_size=1,
+                       token_seq=None, seq_lens=None):
+        """Resolved, compacted rows: (slots int32 [T, k_out], counts int32 [T],
+        masked-entry count)."""
+        topk = _c(topk, np.int32)
+        T, K = topk.shape
+        pt = _c(page_table, np.int32)
+        max_pages = 0 if pt is None else pt.shape[1]
+        out = np.empty((T, k_out), np.int32)
+        counts = np.empty(T, np.int32)
+        err = self.lib.orc_topk_transform(_ptr(topk), T, K,
+                                          _ptr(_c(token_seq, np.int32)), _ptr(pt),
+                                          page_size, max_pages,
+                                          _ptr(_c(seq_lens, np.int32)), num_slots,
+                                          k_out, _ptr(out), _ptr(counts))
+        return out, counts, int(err)
 
     # -- attention -----------------------------------------------------------
     def sparse_attn(self, q, pool, layout, topk, softmax_scale, *,

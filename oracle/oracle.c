@@ -255,6 +255,43 @@ int64_t orc_resolve(const int32_t *topk, int T, int K, const int32_t *token_seq,
     return err;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Index transform ahead of the attention [SCALED, the draft notes: the     */
+/* variable-width page-table transform; Q8, review discussion: prefix       */
+/* requests gather only the referenced context slots through the flattened  */
+/* page-size-1 table, the RAGGED path].                                      */
+/* Readings: every entry is resolved exactly as resolve_slot does for the   */
+/* attention; the row's valid slots are written first, in their input      */
+/* order, then -1 up to the output width k_out (>= k_in); counts[t] is the  */
+/* number of valid slots of row t.  Returns the number of masked entries    */
+/* other than -1 (the attention's error count for the same input).         */
+/* ------------------------------------------------------------------------ */
+int64_t orc_topk_transform(const int32_t *topk, int T, int k_in,
+                           const int32_t *token_seq, const int32_t *page_table,
+                           int page_size, int max_pages,
+                           const int32_t *seq_lens, int64_t num_slots,
+                           int k_out, int32_t *out, int32_t *counts)
+{
+    int64_t err = 0;
+    for (int t = 0; t < T; t++) {
+        int seq = token_seq ? token_seq[t] : t;
+        int32_t *row = out + (int64_t)t * k_out;
+        int n = 0;
+        for (int j = 0; j < k_in; j++) {
+            int64_t slot = resolve_slot(topk[(int64_t)t * k_in + j], seq,
+                                        page_table, page_size, max_pages,
+                                        seq_lens, num_slots, &err);
+            if (slot >= 0)
+                row[n++] = (int32_t)slot;
+        }
+        if (counts)
+            counts[t] = n;
+        for (int j = n; j < k_out; j++)
+            row[j] = -1;
+    }
+    return err;
+}
+
 /* Exact dequantised row value in FP64 [RAW, Modifications: the raw layout  */
 /* is unscaled; SCALED, Motivation: four fp32 scales, one per 128 values].   */
 /* Reading: a scale multiplies its group's decoded values.                  */

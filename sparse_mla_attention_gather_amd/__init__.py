@@ -58,6 +58,9 @@ _ATTN_ARGS = [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32,
               c_int32, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]
 _SIGS["dsa_sparse_attn_decode"] = (c_int32, _ATTN_ARGS)
 _SIGS["dsa_sparse_attn_prefill"] = (c_int32, _ATTN_ARGS)
+_SIGS["dsa_topk_transform"] = (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_int32,
+                                         c_int32, c_int32, c_void_p, c_void_p, c_int64,
+                                         c_void_p, c_int32, c_void_p, c_void_p, c_void_p])
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
     _f.restype = _res
@@ -161,3 +164,12 @@ def dsa_sparse_attn_prefill(q, q_dtype, q_scale, T, H, D, rope_dim, pool,
                  page_table, page_size, max_pages, num_seqs, token_seq,
                  seq_lens, softmax_scale, out, out_dtype, lse, workspace,
                  workspace_bytes, err_count, stream)
+
+
+def dsa_topk_transform(topk, T, k_in, page_table, page_size, max_pages, num_seqs,
+                       token_seq, seq_lens, num_slots, out_slots, k_out,
+                       valid_count=None, err_count=None, stream=None) -> int:
+    return _lib.dsa_topk_transform(_p(topk), T, k_in, _p(page_table), page_size,
+                                   max_pages, num_seqs, _p(token_seq), _p(seq_lens),
+                                   num_slots, _p(out_slots), k_out, _p(valid_count),
+                                   _p(err_count), _s(stream))

@@ -213,6 +213,48 @@ int32_t dsa_quantize_q_fp8(const void *q, int64_t n_elems, int32_t q_dtype,
     return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
 }
 
+int32_t dsa_topk_transform(const int32_t *topk, int32_t T, int32_t k_in,
+                           const int32_t *page_table, int32_t page_size,
+                           int32_t max_pages, int32_t num_seqs,
+                           const int32_t *token_seq, const int32_t *seq_lens,
+                           int64_t num_slots, int32_t *out_slots, int32_t k_out,
+                           int32_t *valid_count, int32_t *err_count, void *stream) {
+    if (T < 0 || k_in < 1 || k_in > 65536) return DSA_ERR_SHAPE;
+    if (k_out < k_in || k_out % 128 != 0 || k_out > 65536) return DSA_ERR_SHAPE;
+    if (num_slots < 0 || num_slots >= ((int64_t)1 << 31)) return DSA_ERR_SHAPE;
+    if (page_table) {
+        if (page_size < 1 || (page_size & (page_size - 1)) != 0 || page_size > (1 << 20))
+            return DSA_ERR_SHAPE;
+        if (max_pages < 1) return DSA_ERR_SHAPE;
+    }
+    if ((page_table || seq_lens) && num_seqs < 1) return DSA_ERR_SHAPE;
+    if ((page_table || seq_lens) && !token_seq && T > num_seqs) return DSA_ERR_SHAPE;
+    if (T == 0) return DSA_OK;
+    if (!topk || !out_slots) return DSA_ERR_NULL;
+    int32_t st = check_device();
+    if (st) return st;
+    dsa::TransformArgs a;
+    a.topk = topk;
+    a.T = T;
+    a.k_in = k_in;
+    a.k_out = k_out;
+    a.page_table = page_table;
+    int shift = 0;
+    if (page_table)
+        while ((1 << shift) < page_size) shift++;
+    a.page_shift = shift;
+    a.max_pages = max_pages;
+    a.num_seqs = num_seqs;
+    a.token_seq = token_seq;
+    a.seq_lens = seq_lens;
+    a.num_slots = num_slots;
+    a.out = out_slots;
+    a.counts = valid_count;
+    a.err_count = err_count;
+    hipError_t e = dsa::launch_topk_transform(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
 size_t dsa_attn_workspace_bytes(int32_t T, int32_t H, int32_t K, int32_t phase) {
     if (T <= 0 || H <= 0 || K <= 0 || K % 128 != 0) return 0;
     return dsa::attn_workspace_bytes(T, H, K, phase);

@@ -181,23 +181,12 @@ __device__ __forceinline__ float sum_over_g(float v) {
 }
 
 // Index resolution of one entry value i, given the page-table word `phys`
-// already fetched for it (see the prologue): -1 -> padding; other invalid
-// values -> masked and counted.
+// already fetched for it (see the prologue).
 __device__ __forceinline__ int32_t resolve_entry(const AttnArgs &a, int32_t i,
                                                  int32_t phys, bool seq_ok,
                                                  int seq_len, bool &err) {
-    err = false;
-    if (i == -1) return -1;
-    err = true;
-    if (i < 0 || !seq_ok || i >= seq_len) return -1;
-    int64_t slot = i;
-    if (a.page_table) {
-        if ((i >> a.page_shift) >= a.max_pages || phys < 0) return -1;
-        slot = ((int64_t)phys << a.page_shift) | (int64_t)(i & ((1 << a.page_shift) - 1));
-    }
-    if (slot >= a.num_slots) return -1;
-    err = false;
-    return (int32_t)slot;
+    return resolve_index(i, phys, seq_ok, seq_len, a.page_table != nullptr, a.page_shift,
+                         a.max_pages, a.num_slots, err);
 }
 
 __device__ __forceinline__ int swz(int row) { return row & 7; }
@@ -927,8 +916,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 vstep(k, I0{});
                 if (k + 1 < n_tiles) vstep(k + 1, I1{});
             }
-            if (!kLate && ((n_tiles - 1) & 1)) pv(n_tiles - 1, I1{});
-            else pv(n_tiles - 1, I0{});
+            if constexpr (kLate) {
+                pv(n_tiles - 1, I0{});
+            } else {
+                if ((n_tiles - 1) & 1) pv(n_tiles - 1, I1{});
+                else pv(n_tiles - 1, I0{});
+            }
             epilogue();
         } else {
             first_tile([&] { read_xc(0); });

@@ -83,6 +83,30 @@ __device__ __forceinline__ f16x8 e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
     return r;
 }
 
+// Resolution of one top-k entry value i (the attention's prologue and the
+// index transform apply the same rule), given the page-table word `phys`
+// already fetched for it: -1 -> padding (not an error); a negative value, a
+// token whose sequence is invalid, i >= seq_len, a page beyond max_pages or
+// a negative page-table word, or a slot >= num_slots -> masked and counted
+// (`err`).  page_shift = log2(page_size); has_pt false: i is the slot.
+__device__ __forceinline__ int32_t resolve_index(int32_t i, int32_t phys, bool seq_ok,
+                                                 int seq_len, bool has_pt, int page_shift,
+                                                 int max_pages, int64_t num_slots,
+                                                 bool &err) {
+    err = false;
+    if (i == -1) return -1;
+    err = true;
+    if (i < 0 || !seq_ok || i >= seq_len) return -1;
+    int64_t slot = i;
+    if (has_pt) {
+        if ((i >> page_shift) >= max_pages || phys < 0) return -1;
+        slot = ((int64_t)phys << page_shift) | (int64_t)(i & ((1 << page_shift) - 1));
+    }
+    if (slot >= num_slots) return -1;
+    err = false;
+    return (int32_t)slot;
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     uint32_t u = __float_as_uint(f);

@@ -48,4 +48,20 @@ size_t attn_workspace_bytes(int T, int H, int K, int phase);
 hipError_t launch_attn(const AttnArgs &a, int layout, bool q_fp8, bool out_bf16,
                        hipStream_t stream);
 
+struct TransformArgs {
+    const int32_t *topk;        // [T, k_in]
+    int T, k_in, k_out;
+    const int32_t *page_table;  // [num_seqs, max_pages] or null
+    int page_shift;             // log2(page_size)
+    int max_pages, num_seqs;
+    const int32_t *token_seq;   // [T] or null
+    const int32_t *seq_lens;    // [num_seqs] or null
+    int64_t num_slots;
+    int32_t *out;               // [T, k_out]
+    int32_t *counts;            // [T] or null
+    int32_t *err_count;         // or null
+};
+
+hipError_t launch_topk_transform(const TransformArgs &a, hipStream_t stream);
+
 }  // namespace dsa

@@ -327,6 +327,67 @@ def pin_resolve_page_boundaries(orc):
                                    9 * 64, 14 * 64 + 63]]) and err == 0
 
 
+def pin_transform_worked_example(orc):
+    """The resolution example above, compacted by hand: each row's valid
+    slots in input order, then -1 to the output width; 5 masked entries."""
+    pt = np.array([[5, 2], [7, -1]], np.int32)
+    topk = np.array([
+        [0, 3, 4, 7, -1, 8, -2, 5],
+        [0, 1, 2, 3, 4, -1, 6, 2],
+    ], np.int32)
+    out, counts, err = orc.topk_transform(topk, 32, 128, page_table=pt, page_size=4,
+                                          token_seq=np.array([0, 1], np.int32),
+                                          seq_lens=np.array([8, 3], np.int32))
+    assert out.shape == (2, 128)
+    assert np.array_equal(out[0, :5], [20, 23, 8, 11, 9]) and np.all(out[0, 5:] == -1)
+    assert np.array_equal(out[1, :4], [28, 29, 30, 30]) and np.all(out[1, 4:] == -1)
+    assert np.array_equal(counts, [5, 4]) and err == 5
+
+
+def pin_transform_identity_table(orc):
+    """Special case: page size 1 and page_table[s][p] = p, so a slot is its
+    position; the output is then numpy's boolean compaction of each row's
+    non-negative positions, for widths that are and are not multiples of
+    128, with padding of any length and all-padding rows."""
+    rng = np.random.default_rng(5)
+    for T, k_in, k_out in ((3, 1, 128), (4, 100, 128), (5, 1000, 1024), (2, 2048, 4096)):
+        n_pos = 5000
+        topk = rng.integers(0, n_pos, (T, k_in)).astype(np.int32)
+        topk[rng.random((T, k_in)) < 0.3] = -1
+        topk[0] = -1
+        pt = np.tile(np.arange(n_pos, dtype=np.int32), (T, 1))
+        out, counts, err = orc.topk_transform(topk, n_pos, k_out, page_table=pt, page_size=1)
+        assert err == 0
+        for t in range(T):
+            want = topk[t][topk[t] >= 0]
+            assert counts[t] == len(want)
+            assert np.array_equal(out[t, :len(want)], want)
+            assert np.all(out[t, len(want):] == -1)
+
+
+def pin_transform_shifted_table(orc):
+    """Closed form: page_table[s][p] = p + 3 with page size 64 puts position
+    i at slot i + 192; positions >= seq_len, below -1, or on pages beyond
+    the table are dropped and counted; -1 is dropped and not counted."""
+    rng = np.random.default_rng(6)
+    T, k_in, P_, pages = 6, 700, 64, 20
+    pt = np.tile(np.arange(pages, dtype=np.int32) + 3, (T, 1))
+    seq_lens = rng.integers(200, pages * P_ + 300, T).astype(np.int32)
+    topk = rng.integers(-3, pages * P_ + 200, (T, k_in)).astype(np.int32)
+    out, counts, err = orc.topk_transform(topk, (pages + 3) * P_, 768, page_table=pt,
+                                          page_size=P_, seq_lens=seq_lens)
+    want_err = 0
+    for t in range(T):
+        row = topk[t]
+        ok = (row >= 0) & (row < seq_lens[t]) & (row < pages * P_)
+        want = row[ok] + 3 * P_
+        want_err += int(np.sum((row != -1) & ~ok))
+        assert counts[t] == len(want)
+        assert np.array_equal(out[t, :len(want)], want)
+        assert np.all(out[t, len(want):] == -1)
+    assert err == want_err
+
+
 # --------------------------------------------------------------------------
 # attention
 # --------------------------------------------------------------------------

@@ -235,6 +235,47 @@ def test_quantize_rejections():
 
 # ------------------------------------------------------------------ build check
 
+def transform_call(**over):
+    args = dict(topk=FAKE, T=4, k_in=2048, page_table=FAKE, page_size=64,
+                max_pages=128, num_seqs=4, token_seq=None, seq_lens=FAKE,
+                num_slots=1 << 20, out_slots=FAKE, k_out=2048, valid_count=None,
+                err_count=None, stream=0)
+    args.update(over)
+    return dsa.dsa_topk_transform(**args)
+
+
+TRANSFORM_REJECT = [
+    (dict(k_in=0), "DSA_ERR_SHAPE"),
+    (dict(k_in=65537, k_out=65536), "DSA_ERR_SHAPE"),
+    (dict(k_out=2000), "DSA_ERR_SHAPE"),          # not a multiple of 128
+    (dict(k_in=1000, k_out=896), "DSA_ERR_SHAPE"),  # narrower than the input
+    (dict(k_out=65536 + 128), "DSA_ERR_SHAPE"),
+    (dict(T=-1), "DSA_ERR_SHAPE"),
+    (dict(page_size=48), "DSA_ERR_SHAPE"),
+    (dict(max_pages=0), "DSA_ERR_SHAPE"),
+    (dict(num_seqs=0), "DSA_ERR_SHAPE"),
+    (dict(T=5), "DSA_ERR_SHAPE"),                 # more tokens than sequences
+    (dict(num_slots=-1), "DSA_ERR_SHAPE"),
+    (dict(num_slots=1 << 31), "DSA_ERR_SHAPE"),
+    (dict(topk=None), "DSA_ERR_NULL"),
+    (dict(out_slots=None), "DSA_ERR_NULL"),
+]
+
+
+@pytest.mark.parametrize("over,status", TRANSFORM_REJECT,
+                         ids=[str(o) for o, _ in TRANSFORM_REJECT])
+def test_transform_rejections(over, status):
+    assert transform_call(**over) == getattr(dsa, status)
+
+
+def test_transform_accepts_any_input_width():
+    # widths that are not multiples of 128 pass validation (the call then
+    # stops at the device check: no GPU in this container)
+    for k_in, k_out in ((1, 128), (100, 128), (1000, 1024), (2047, 2048), (3000, 4096)):
+        assert transform_call(k_in=k_in, k_out=k_out) in (dsa.DSA_ERR_DEVICE, dsa.DSA_OK)
+    assert transform_call(T=0, topk=None, out_slots=None) == dsa.DSA_OK
+
+
 def test_build_rejects_kernels_that_use_scratch():
     """The build refuses kernels with spills or scratch: the attention kernel
     counts outstanding vector-memory operations to wait for its tile copies."""

@@ -81,6 +81,12 @@ MUTANTS = [
      "x + (int64_t)nv * ORC_D, ORC_D * sizeof(double)) != 0) nv++;\n"),
     ("token_sequence_ignored", "int seq = jb->token_seq ? jb->token_seq[t] : t;",
      "int seq = jb->token_seq ? 0 : t;"),
+    ("transform_keeps_masked", "            if (slot >= 0)\n                row[n++] = (int32_t)slot;",
+     "            if (slot >= -1)\n                row[n++] = (int32_t)slot;"),
+    ("transform_reverses", "row[n++] = (int32_t)slot;", "row[k_in - 1 - n++] = (int32_t)slot;"),
+    ("transform_pads_zero", "        for (int j = n; j < k_out; j++)\n            row[j] = -1;",
+     "        for (int j = n; j < k_out; j++)\n            row[j] = 0;"),
+    ("transform_count_off", "counts[t] = n;", "counts[t] = n + (t & 1);"),
 ]
 
 
