@@ -276,15 +276,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     constexpr int kGpp = kDP / 128;              // scale groups per part
     constexpr int kChunks = kDP / 16;            // 16-byte row chunks per part
     constexpr int kXc = kDP / 64;                // of which one lane holds (4 lane groups)
-    // Schedule.  Pipelined (16 heads; 32 heads with FP8 queries): waves 0-7
-    // score (QK over every head tile, and the owners' softmax), waves 8-15
-    // accumulate PV one tile behind, so the owners' softmax of tile k
-    // overlaps the PV of tile k-1 and each tile's operand reads overlap the
-    // phase before.  Sequential (32 heads with bf16 queries, whose 64
-    // registers of query per scoring lane would not fit the 128 a lane has
-    // at 16 waves per CU): every wave scores and accumulates, each tile
-    // read, scored, normalised and accumulated in turn.
-    constexpr bool kPipe = NT == 1 || QFP8;
+    // Schedule.  Pipelined: waves 0-7 score (QK and the owners' softmax),
+    // waves 8-15 accumulate PV one tile behind, so the owners' softmax of
+    // tile k overlaps the PV of tile k-1 and each tile's operand reads
+    // overlap the phase before.  Sequential (kept for comparison, with
+    // DSA_SEQUENTIAL for 32-head blocks): every wave scores and accumulates,
+    // each tile read, scored, normalised and accumulated in turn.
+#ifdef DSA_SEQUENTIAL
+    constexpr bool kPipe = NT == 1;
+#else
+    constexpr bool kPipe = true;
+#endif
     static_assert(kParts == 2, "one publishing wave per head tile and quarter");
     constexpr bool kLate = kPipe && NT == 2;     // PV operands read in their own step
     constexpr int kDT = kPipe ? 4 : 2;           // PV: 16-dim tiles per wave
@@ -297,17 +299,31 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
-    const int wq = w & 3;                        // QK: entries 16 wq .. +16 of the tile
-    const int dp = (w >> 2) % kParts;            // QK: dims part
     const bool is_v = kPipe && w >= 8;           // pipelined: a PV-only wave
-    // Scoring.  Pipelined: a scoring wave computes dims part dp of every head
-    // tile; head tile ht is owned (parts added, P formed) by the waves with
-    // dp == ht, and the other part's wave publishes its partial.  16 heads:
-    // the dp = 1 waves only publish.  Sequential: wave w scores head tile
-    // (w >> 2) / kParts only, and the dp = 0 waves own it.
-    const int ht = kPipe ? (NT == 1 ? 0 : dp) : (w >> 2) / kParts;
-    const bool owner = !is_v && (kPipe ? (NT == 1 ? dp == 0 : true) : dp == 0);
-    constexpr int kQT = kPipe ? NT : 1;          // head tiles a scoring wave scores
+    // Scoring (partials of 16 entries x 16 heads x one 256-dim part dp;
+    // entry quarter q and head tile ht are owned -- parts added, P formed --
+    // by one wave, to which the wave holding the other part publishes its
+    // partial through LDS slot ht*4 + q):
+    //   16 heads: wave (q = w & 3, dp = w >> 2) scores quarter q; the dp = 0
+    //     waves own their quarter, the dp = 1 waves only publish;
+    //   32 heads, FP8 query: wave (q, dp) scores quarter q of both head
+    //     tiles (each converted row operand feeds two MFMAs) and owns head
+    //     tile dp;
+    //   32 heads, bf16 query (kRowPair: the query of both head tiles would
+    //     not fit the 128 registers a lane has at 16 waves per CU): wave
+    //     (rh = w & 1, dp = (w >> 1) & 1, ht = w >> 2) scores quarters 2rh
+    //     and 2rh + 1 of head tile ht and owns quarter 2rh + dp;
+    //   sequential: wave w scores quarter w & 3 of head tile (w >> 2) /
+    //     kParts, and the dp = 0 waves own it.
+    constexpr bool kRowPair = kPipe && NT == 2 && !QFP8;
+    constexpr int kRT = kRowPair ? 2 : 1;        // entry quarters a scoring wave scores
+    constexpr int kQT = kRowPair ? 1 : (kPipe ? NT : 1);   // head tiles it scores
+    const int rh = w & 1;
+    const int dp = kRowPair ? (w >> 1) & 1 : (w >> 2) % kParts;      // QK: dims part
+    const int wq = kRowPair ? 2 * rh + dp : w & 3;   // entry quarter owned (and scored)
+    const int ht = kRowPair ? (w >> 2) & 1
+                            : (kPipe ? (NT == 1 ? 0 : dp) : (w >> 2) / kParts);
+    const bool owner = !is_v && (kRowPair || (kPipe ? (NT == 1 ? dp == 0 : true) : dp == 0));
     const int dbase = kPipe ? 64 * (w - 8) : 32 * w;   // PV: first of this wave's dims
     const int n_hb = (a.H + kHB - 1) / kHB;
 
@@ -343,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     if (!is_v) {
 #pragma unroll
         for (int nt = 0; nt < kQT; nt++) {
-            const int h = hb * kHB + (kPipe ? nt : ht) * 16 + c;
+            const int h = hb * kHB + ((kPipe && !kRowPair) ? nt : ht) * 16 + c;
             const int64_t qrow = ((int64_t)t * a.H + (h < a.H ? h : 0)) * kD;
             if constexpr (QFP8) {
                 const uint8_t *qp = reinterpret_cast<const uint8_t *>(a.q) + qrow + dp * kDP + g * 32;
@@ -479,9 +495,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // Operands of a tile in registers: the QK row chunks (xc) of the tile
     // being scored, the PV transpose reads (tv) of the last two tiles (by
     // tile parity; one set when not pipelined or with kLate).
-    u32x4 xc[kXc];
+    u32x4 xc[kRT][kXc];
     u32x2 tv[kPipe && !kLate ? 2 : 1][2][kDT];
-    f32x4 part[kQT];
+    f32x4 part[kRT * kQT];      // [entry quarter][head tile]
 
     // Wait until this wave's DMA of tile j has landed: `issued` is the last
     // tile issued so far, later tiles may still be in flight.
@@ -497,14 +513,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // the halves of chunk dp*kChunks + 4m + g, FP8 steps k2 the chunk pair
     // dp*kChunks + 8 k2 + 2g, +1 (a step never leaves a 128-wide scale group).
     auto read_xc = [&](int j) {
-        const int r = 16 * wq + c;
-        const uint8_t *xr = lds + (j % kNBuf) * L::kBufBytes + r * 512;
-        const int sw = swz(r);
 #pragma unroll
-        for (int m = 0; m < kXc; m++) {
-            const int ch = QFP8 ? dp * kChunks + (m >> 1) * 8 + g * 2 + (m & 1)
-                                : dp * kChunks + m * 4 + g;
-            xc[m] = *reinterpret_cast<const u32x4 *>(xr + ((ch ^ sw) * 16));
+        for (int rt = 0; rt < kRT; rt++) {
+            const int r = 16 * (kRowPair ? 2 * rh + rt : wq) + c;
+            const uint8_t *xr = lds + (j % kNBuf) * L::kBufBytes + r * 512;
+            const int sw = swz(r);
+#pragma unroll
+            for (int m = 0; m < kXc; m++) {
+                const int ch = QFP8 ? dp * kChunks + (m >> 1) * 8 + g * 2 + (m & 1)
+                                    : dp * kChunks + m * 4 + g;
+                xc[rt][m] = *reinterpret_cast<const u32x4 *>(xr + ((ch ^ sw) * 16));
+            }
         }
     };
     // PV operand X^T of tile j via transpose reads: lane (c, g) addresses
@@ -546,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 f32x4 accg[kSteps8];
 #pragma unroll
                 for (int k2 = 0; k2 < kSteps8; k2++) {
-                    const u32x4 &lo = xc[2 * k2], &hi = xc[2 * k2 + 1];
+                    const u32x4 &lo = xc[0][2 * k2], &hi = xc[0][2 * k2 + 1];
                     const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
                     accg[k2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -562,44 +581,61 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 }
             }
         } else {
-            // raw rows: two independent chains (even / odd kk) for one head
-            // tile, one per head tile for two; scaled rows (one head tile):
-            // one chain per 128-wide scale group
+            // raw rows: two independent chains (even / odd kk) for a single
+            // (quarter, head tile) product, else one per product; scaled
+            // rows (one of each): one chain per 128-wide scale group
             constexpr int kCh = (LAYOUT == 0 && kQT > 1) ? 1 : 2;
-            f32x4 accg[kQT][2];
+            f32x4 accg[kRT][kQT][2];
 #pragma unroll
-            for (int nt = 0; nt < kQT; nt++) accg[nt][0] = accg[nt][1] = f32x4{0, 0, 0, 0};
+            for (int rt = 0; rt < kRT; rt++)
 #pragma unroll
-            for (int kk = 0; kk < kSteps; kk++) {
-                const u32x4 &ch = xc[kk >> 1];
-                const bf16x8 av = (kk & 1) ? e4m3x8_to_bf16(ch[2], ch[3])
-                                           : e4m3x8_to_bf16(ch[0], ch[1]);
-                const int q = LAYOUT == 0 ? (kCh == 2 ? (kk & 1) : 0)
-                                          : (kGpp == 1 ? (kk & 1) : (kk >> 2));
+                for (int nt = 0; nt < kQT; nt++) accg[rt][nt][0] = accg[rt][nt][1] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int rt = 0; rt < kRT; rt++)
+#pragma unroll
+                for (int kk = 0; kk < kSteps; kk++) {
+                    const int q = LAYOUT == 0 ? (kCh == 2 ? (kk & 1) : 0)
+                                              : (kGpp == 1 ? (kk & 1) : (kk >> 2));
+                    const u32x4 &ch = xc[rt][kk >> 1];
+                    const bf16x8 av = (kk & 1) ? e4m3x8_to_bf16(ch[2], ch[3])
+                                               : e4m3x8_to_bf16(ch[0], ch[1]);
+#pragma unroll
+                    for (int nt = 0; nt < kQT; nt++)
+                        accg[rt][nt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            av, bq[nt][kk], accg[rt][nt][q], 0, 0, 0);
+                    // two quarters: each step's converts stay next to its
+                    // MFMAs (hoisted ahead, the converted operands would not
+                    // fit the registers beside both quarters' rows)
+                    if constexpr (kRT > 1) __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+            for (int rt = 0; rt < kRT; rt++)
 #pragma unroll
                 for (int nt = 0; nt < kQT; nt++)
-                    accg[nt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[nt][kk], accg[nt][q], 0, 0, 0);
-            }
 #pragma unroll
-            for (int nt = 0; nt < kQT; nt++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    if constexpr (LAYOUT == 0 || kGpp == 1) {
-                        const float s = kCh == 2 ? accg[nt][0][i] + accg[nt][1][i] : accg[nt][0][i];
-                        part[nt][i] = LAYOUT == 0 ? s : s * scv[i][0];
-                    } else {
-                        part[nt][i] = accg[nt][0][i] * scv[i][0] + accg[nt][1][i] * scv[i][kGpp - 1];
+                    for (int i = 0; i < 4; i++) {
+                        const f32x4 *ag = accg[rt][nt];
+                        if constexpr (LAYOUT == 0 || kGpp == 1) {
+                            const float s = kCh == 2 ? ag[0][i] + ag[1][i] : ag[0][i];
+                            part[rt * kQT + nt][i] = LAYOUT == 0 ? s : s * scv[i][0];
+                        } else {
+                            part[rt * kQT + nt][i] = ag[0][i] * scv[i][0] + ag[1][i] * scv[i][kGpp - 1];
+                        }
                     }
-                }
         }
+        // publish every partial this wave does not own
 #pragma unroll
-        for (int nt = 0; nt < kQT; nt++) {
-            const int qt = kPipe ? nt : ht;          // head tile of part[nt]
-            if (!(owner && qt == ht)) {
-                const int slot = qt * 4 + wq;
-                *reinterpret_cast<f32x4 *>(sp_lds + (slot * 16 + c) * 16 + 4 * sp_slot(g, c)) = part[nt];
+        for (int rt = 0; rt < kRT; rt++)
+#pragma unroll
+            for (int nt = 0; nt < kQT; nt++) {
+                const int qt = (kPipe && !kRowPair) ? nt : ht;   // its head tile
+                const int qq = kRowPair ? 2 * rh + rt : wq;        // its entry quarter
+                if (!(owner && qt == ht && qq == wq)) {
+                    const int slot = qt * 4 + qq;
+                    *reinterpret_cast<f32x4 *>(sp_lds + (slot * 16 + c) * 16 + 4 * sp_slot(g, c)) =
+                        part[rt * kQT + nt];
+                }
             }
-        }
     };
 
     // Owner waves, tile j: full scores of entries 16 wq + 4g + i, head ht*16
@@ -615,8 +651,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         uint8_t *p_w = lds + L::kOffP + par * L::kPBytes;
         const int hh = ht * 16 + c;
         const int4 sl4 = *reinterpret_cast<const int4 *>(slots + j * kTile + 16 * wq + 4 * g);
-        // own part of the owned head tile plus the other part's, published
-        f32x4 s = (kQT == 1 || ht == 0) ? part[0] : part[kQT - 1];
+        // own part of the owned (quarter, head tile) plus the other part's,
+        // published
+        f32x4 s;
+        if constexpr (kRowPair) s = dp == 0 ? part[0] : part[1];
+        else s = (kQT == 1 || ht == 0) ? part[0] : part[kQT - 1];
         {
             const int slot = ht * 4 + wq;
             s += *reinterpret_cast<const f32x4 *>(sp_lds + (slot * 16 + c) * 16 + 4 * sp_slot(g, c));
@@ -790,7 +829,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // denominators: the owner lanes' shares, then the four quarters weighted
     // by 2^(m_q - m_ref); the quarter maxima are the last tile's.  Output or
     // partial state from the waves that hold O.
-    auto epilogue = [&]() {
+    // SCORING (compile-time): called by the pipelined scoring waves, which
+    // only publish their denominators (O, which they never touch, is then
+    // not live in their code).
+    auto epilogue = [&](auto scoring) {
         const float *mq_fin = reinterpret_cast<const float *>(
             lds + L::kOffMq + ((n_tiles - 1) & 1) * L::kMqBytes);
         if (owner) {
@@ -798,7 +840,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             if (g == 0) rl_lds[(ht * 16 + c) * 4 + wq] = l_part;
         }
         __syncthreads();
-        if (kPipe && !is_v) return;           // the PV waves hold O
+        if constexpr (decltype(scoring)::value) return;   // the PV waves hold O
         const int w_first = kPipe ? 8 : 0;    // writes m, l and lse
 #pragma unroll
         for (int nt = 0; nt < NT; nt++) {
@@ -922,21 +964,26 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 if ((n_tiles - 1) & 1) pv(n_tiles - 1, I1{});
                 else pv(n_tiles - 1, I0{});
             }
-            epilogue();
+            epilogue(std::false_type{});
         } else {
-            first_tile([&] { read_xc(0); });
+            // (kRowPair: a tile's row chunks are read in its own step, not
+            // prefetched during the softmax before, so that they are not live
+            // beside the softmax; the tile's buffer outlives the step)
+            first_tile([&] { if constexpr (!kRowPair) read_xc(0); });
             for (int k = 0; k < n_tiles; k++) {
                 const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + 1 + kAhead, n_tiles - 1) * kTile, w, lane);
+                if constexpr (kRowPair) read_xc(k);
                 qk(k);
                 wait_tile(k + 1, k + kAhead);
                 barrier_raw();
-                if (owner) softmax(k, [&] { if (k + 1 < n_tiles) read_xc(k + 1); });
-                else if (k + 1 < n_tiles) read_xc(k + 1);
+                const bool pre = !kRowPair && k + 1 < n_tiles;
+                if (owner) softmax(k, [&] { if (pre) read_xc(k + 1); });
+                else if (pre) read_xc(k + 1);
                 wait_lgkm0();
                 barrier_raw();
                 refill(k, nsl);
             }
-            epilogue();
+            epilogue(std::true_type{});
         }
     } else {
         // P and the quarter maxima alternate between two buffers by tile
@@ -961,7 +1008,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             barrier_raw();
             pv(k, I0{});
         }
-        epilogue();
+        epilogue(std::false_type{});
     }
 
 }
