@@ -433,17 +433,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             const int j = tid + i * kThreads;
             bool err;
             const int32_t s = resolve_entry(a, v[i], phys[i], seq_ok, seq_len, err);
-            n_err += err;
+            n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(err));   // the wave's
             if (j < n_ent) slots[j] = s;
             const uint64_t vb = __builtin_amdgcn_ballot_w64(j < n_ent && s >= 0);
             if (vb) last = max(last, w * 64 + 63 - (int)__builtin_clzll(vb) + i * kThreads);
         }
         if (lane == 0) reinterpret_cast<int *>(rl_lds)[w] = last;
-        if (a.err_count && hb == 0) {
-#pragma unroll
-            for (int s = 1; s < 64; s <<= 1) n_err += __shfl_xor(n_err, s);
-            if (lane == 0 && n_err) atomicAdd(a.err_count, n_err);
-        }
+        if (a.err_count && hb == 0 && lane == 0 && n_err) atomicAdd(a.err_count, n_err);
     }
     // slots visible; also drains the query and index loads, so that inside
     // the loop the only outstanding vector-memory operations are tile DMAs
