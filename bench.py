@@ -61,7 +61,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus N with N > 1 "
+        print("bench.py: this library runs on exactly one GPU; --gpus N with N > 1 "
               "is not supported (no sharding or collectives on this path)",
               file=sys.stderr)
         sys.exit(2)

@@ -21,8 +21,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-RAW, SCALED = 0, 1
-ROW_BYTES = {RAW: 512, SCALED: 528}
+RAW, SCALED, ROPE = 0, 1, 2
+ROW_BYTES = {RAW: 512, SCALED: 528, ROPE: 656}
+ROPE_DIM = 64
 
 
 def build(src: str = SRC, out: str = LIB, extra_flags: tuple = ()) -> str:
@@ -98,10 +99,12 @@ class Oracle:
 
     # -- writer --------------------------------------------------------------
     def kv_write(self, kv_bf16, slot_mapping, pool, layout: int) -> int:
-        """Write rows of ``kv_bf16`` (uint16 bf16 bits, [n, >=512]) into ``pool``
-        (uint8 [num_slots, row_bytes], modified in place).  Returns errors."""
+        """Write rows of ``kv_bf16`` (uint16 bf16 bits, [n, >=512], or
+        [n, >=576] for 656-byte rows) into ``pool`` (uint8 [num_slots,
+        row_bytes], modified in place).  Returns errors."""
         kv = np.asarray(kv_bf16)
-        assert kv.dtype == np.uint16 and kv.ndim == 2 and kv.shape[1] >= 512
+        assert kv.dtype == np.uint16 and kv.ndim == 2
+        assert kv.shape[1] >= 512 + (ROPE_DIM if layout == ROPE else 0)
         assert kv.strides[1] == 2
         sm = _c(slot_mapping, np.int64)
         assert pool.dtype == np.uint8 and pool.flags.c_contiguous
@@ -159,12 +162,14 @@ class Oracle:
                     token_seq=None, seq_lens=None, nthreads=None):
         """Returns (out f64 [T,H,512], lse f64 [T,H], err_count).
 
-        ``q`` is uint16 bf16 bits [T,H,512], or uint8 FP8 codes when
-        ``q_scale`` is given."""
+        ``q`` is uint16 bf16 bits [T,H,512] ([T,H,576] for 656-byte rows:
+        latent then RoPE part), or uint8 FP8 codes when ``q_scale`` is
+        given."""
         is_fp8 = q_scale is not None
         q = _c(q, np.uint8 if is_fp8 else np.uint16)
-        T, H, D = q.shape
-        assert D == 512
+        T, H, Dq = q.shape
+        D = 512
+        assert Dq == D + (ROPE_DIM if layout == ROPE else 0)
         topk = _c(topk, np.int32)
         assert topk.shape[0] == T
         K = topk.shape[1]

@@ -32,6 +32,12 @@
 #define ORC_GROUP 128      /* elements per scale group in the 528-byte row        */
 #define ORC_RAW_BYTES 512  /* raw row: 512 unscaled FP8 values [RAW, Speed Tests]  */
 #define ORC_SCALED_BYTES 528 /* 512 FP8 + 4 fp32 scales [SCALED, Motivation]      */
+/* RoPE row [SCALED, Motivation: the existing helpers require a 656-byte    */
+/* RoPE layout].  Reading (the pages give only the size): the 528-byte      */
+/* scaled row followed by 64 bf16 RoPE values, little-endian; the query is  */
+/* then 512 + 64 wide and the RoPE part adds q_rope . k_rope to the score.  */
+#define ORC_ROPE 64
+#define ORC_ROPE_BYTES 656
 
 /* ------------------------------------------------------------------------ */
 /* FP8 E4M3FN (OCP): sign | 4 exponent bits (bias 7) | 3 mantissa bits.      */
@@ -119,13 +125,16 @@ static float bf16_to_f32(uint16_t h)
 /*       s_g = fp32(amax_g / 448) (1.0 if amax_g == 0),                    */
 /*       byte[d] = E4M3(fp32(x[d] / s_g)), scales stored little-endian fp32 */
 /*       at row bytes 512 + 4g.                                             */
+/*   RoPE (layout 2): input rows of 512 + 64 values; the first 512 as the   */
+/*       scaled layout, the 64 RoPE values copied as bf16 to bytes 528..655. */
 /* ------------------------------------------------------------------------ */
 int64_t orc_kv_write(const uint16_t *kv, int64_t n, int64_t kv_row_stride,
                      const int64_t *slot_mapping, uint8_t *pool,
                      int64_t num_slots, int layout)
 {
     int64_t errors = 0;
-    int64_t row_bytes = layout == 0 ? ORC_RAW_BYTES : ORC_SCALED_BYTES;
+    int64_t row_bytes = layout == 0 ? ORC_RAW_BYTES
+                        : layout == 1 ? ORC_SCALED_BYTES : ORC_ROPE_BYTES;
 
     for (int64_t i = 0; i < n; i++) {
         int64_t slot = slot_mapping[i];
@@ -157,6 +166,11 @@ int64_t orc_kv_write(const uint16_t *kv, int64_t n, int64_t kv_row_stride,
                 }
                 memcpy(dst + ORC_D + 4 * g, &scale, 4);
             }
+            if (layout == 2)
+                for (int r = 0; r < ORC_ROPE; r++) {
+                    dst[ORC_SCALED_BYTES + 2 * r] = (uint8_t)(src[ORC_D + r] & 0xff);
+                    dst[ORC_SCALED_BYTES + 2 * r + 1] = (uint8_t)(src[ORC_D + r] >> 8);
+                }
         }
     }
     return errors;
@@ -294,7 +308,15 @@ int64_t orc_topk_transform(const int32_t *topk, int T, int k_in,
 
 /* Exact dequantised row value in FP64 [RAW, Modifications: the raw layout  */
 /* is unscaled; SCALED, Motivation: four fp32 scales, one per 128 values].   */
-/* Reading: a scale multiplies its group's decoded values.                  */
+/* Reading: a scale multiplies its group's decoded values.  The RoPE part   */
+/* of a 656-byte row (its bf16 values, exact in FP64) goes to xr.           */
+static void rope_row(const uint8_t *row, double *xr)
+{
+    for (int r = 0; r < ORC_ROPE; r++)
+        xr[r] = bf16_to_f32((uint16_t)(row[ORC_SCALED_BYTES + 2 * r] |
+                                       (row[ORC_SCALED_BYTES + 2 * r + 1] << 8)));
+}
+
 static void dequant_row(const uint8_t *row, int layout, double *x)
 {
     if (layout == 0) {
@@ -314,6 +336,7 @@ static void dequant_row(const uint8_t *row, int layout, double *x)
 /* latent-512 / RoPE-0 queries].  The 512-wide latent row is both key and   */
 /* value.  For token t, head h, over the multiset of valid entries j:       */
 /*   s_j   = softmax_scale * sum_d qhat[h][d] * x_j[d]                      */
+/*           (656-byte rows: + softmax_scale * sum_r qhat[h][512+r] * xr_j[r]) */
 /*   o     = sum_j exp(s_j - M) x_j / sum_j exp(s_j - M),  M = max_j s_j   */
 /*   lse   = M + log(sum_j exp(s_j - M))                                    */
 /* Two passes (max, then weights): deliberately not an online softmax.     */
@@ -343,9 +366,12 @@ struct attn_job {
 
 static void attn_tokens(struct attn_job *jb)
 {
-    int64_t row_bytes = jb->layout == 0 ? ORC_RAW_BYTES : ORC_SCALED_BYTES;
+    int64_t row_bytes = jb->layout == 0 ? ORC_RAW_BYTES
+                        : jb->layout == 1 ? ORC_SCALED_BYTES : ORC_ROPE_BYTES;
+    int rope = jb->layout == 2 ? ORC_ROPE : 0;   /* query row: ORC_D + rope */
     double *x = malloc(sizeof(double) * (size_t)jb->K * ORC_D);
-    double *qh = malloc(sizeof(double) * ORC_D);
+    double *xr = malloc(sizeof(double) * (size_t)jb->K * ORC_ROPE);
+    double *qh = malloc(sizeof(double) * (ORC_D + ORC_ROPE));
     double *s = malloc(sizeof(double) * (size_t)jb->K);
 
     for (int t = jb->t_begin; t < jb->t_end; t++) {
@@ -362,15 +388,17 @@ static void attn_tokens(struct attn_job *jb)
                 continue;
             dequant_row(jb->pool + sl * row_bytes, jb->layout,
                         x + (int64_t)nv * ORC_D);
+            if (rope)
+                rope_row(jb->pool + sl * row_bytes, xr + (int64_t)nv * ORC_ROPE);
             nv++;
         }
 
         for (int h = 0; h < jb->H; h++) {
-            int64_t qoff = ((int64_t)t * jb->H + h) * ORC_D;
-            double *o = jb->out + qoff;
+            int64_t qoff = ((int64_t)t * jb->H + h) * (ORC_D + rope);
+            double *o = jb->out + ((int64_t)t * jb->H + h) * ORC_D;
             double M = -INFINITY, L = 0.0;
 
-            for (int d = 0; d < ORC_D; d++) {
+            for (int d = 0; d < ORC_D + rope; d++) {
                 if (jb->q_is_fp8)
                     qh[d] = orc_fp8_decode(((const uint8_t *)jb->q)[qoff + d]) *
                             (double)jb->q_scale;
@@ -381,6 +409,8 @@ static void attn_tokens(struct attn_job *jb)
                 double dot = 0.0;
                 for (int d = 0; d < ORC_D; d++)
                     dot += qh[d] * x[(int64_t)j * ORC_D + d];
+                for (int r = 0; r < rope; r++)
+                    dot += qh[ORC_D + r] * xr[(int64_t)j * ORC_ROPE + r];
                 s[j] = (double)jb->softmax_scale * dot;
                 if (s[j] > M)
                     M = s[j];
@@ -405,6 +435,7 @@ static void attn_tokens(struct attn_job *jb)
         }
     }
     free(x);
+    free(xr);
     free(qh);
     free(s);
 }

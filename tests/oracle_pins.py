@@ -19,7 +19,7 @@ import torch
 import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-RAW, SCALED = 0, 1
+RAW, SCALED, ROPE = 0, 1, 2
 
 
 # --------------------------------------------------------------------------
@@ -406,18 +406,25 @@ def build_pool(orc, wl: W.Workload, poison=True):
         orc.kv_write(lat, slots, pool, RAW)
     else:
         tmp = np.zeros((len(slots), 512), np.uint8)
-        orc.kv_write(lat, np.arange(len(slots)), tmp, RAW)
+        orc.kv_write(lat[:, :512], np.arange(len(slots)), tmp, RAW)
         pool[slots, :512] = tmp
-        pool[slots, 512:] = sc.view(np.uint8).reshape(len(slots), 16)
+        pool[slots, 512:528] = sc.view(np.uint8).reshape(len(slots), 16)
+        if wl.layout == ROPE:      # the RoPE values as little-endian bf16
+            pool[slots, 528:656] = np.ascontiguousarray(lat[:, 512:]).view(np.uint8)
     return pool
 
 
 def dequant_pool(pool, layout):
     x = torch_dec(pool[:, :512])
-    if layout == SCALED:
-        sc = pool[:, 512:].copy().view(np.float32).astype(np.float64)
+    if layout in (SCALED, ROPE):
+        sc = pool[:, 512:528].copy().view(np.float32).astype(np.float64)
         x = x * np.repeat(sc, 128, axis=1)
     return x
+
+
+def rope_pool(pool):
+    """The RoPE values of 656-byte rows, fp64 [slots, 64]."""
+    return f32_from_bf16(np.ascontiguousarray(pool[:, 528:656]).view(np.uint16)).astype(np.float64)
 
 
 def count_matrix(wl: W.Workload):
@@ -444,9 +451,11 @@ def count_matrix(wl: W.Workload):
     return C
 
 
-def dense_attention(qhat, X, C, scale):
-    """Full attention over every slot, each weighted by its multiplicity."""
+def dense_attention(qhat, X, C, scale, Xk=None):
+    """Full attention over every slot, each weighted by its multiplicity.
+    Keys are Xk (default X: the latent row is both key and value)."""
     T, H, _ = qhat.shape
+    Xk = X if Xk is None else Xk
     out = np.zeros((T, H, 512))
     lse = np.full((T, H), -np.inf)
     for t in range(T):
@@ -454,7 +463,7 @@ def dense_attention(qhat, X, C, scale):
         if not live.any():
             continue
         Xl = X[live]
-        s = float(scale) * (qhat[t] @ Xl.T)           # [H, n]
+        s = float(scale) * (qhat[t] @ Xk[live].T)     # [H, n]
         M = s.max(axis=1, keepdims=True)
         w = C[t, live][None, :] * np.exp(s - M)
         L = w.sum(axis=1, keepdims=True)
@@ -492,6 +501,84 @@ def pin_attention_dense_brute_force(orc):
                                        count_matrix(wl), wl.softmax_scale)
         _close(out, ref)
         _close(lse, ref_lse)
+
+
+def pin_writer_rope(orc):
+    """656-byte rows: bytes 0..527 are exactly the 528-byte writer's bytes of
+    the first 512 values, bytes 528..655 the 64 RoPE values' bf16 bit
+    patterns, little-endian (numpy's view of the input)."""
+    rng = np.random.default_rng(71)
+    n = 40
+    kv = W.normal_bf16(rng, (n, 576))
+    kv[3, 512:] = 0
+    kv[5, :512] = 0
+    slots = rng.permutation(64)[:n].astype(np.int64)
+    slots[7] = -1
+    rope = np.full((64, 656), 0xAB, np.uint8)
+    scaled = np.full((64, 528), 0xAB, np.uint8)
+    assert orc.kv_write(kv, slots, rope, ROPE) == 0
+    assert orc.kv_write(np.ascontiguousarray(kv[:, :512]), slots, scaled, SCALED) == 0
+    assert np.array_equal(rope[:, :528], scaled)
+    ok = slots >= 0
+    assert np.array_equal(rope[slots[ok], 528:], np.ascontiguousarray(kv[ok, 512:]).view(np.uint8))
+    untouched = np.setdiff1d(np.arange(64), slots[ok])
+    assert np.all(rope[untouched] == 0xAB)
+
+
+def pin_attention_rope_dense_brute_force(orc):
+    """656-byte rows against dense attention over every slot: keys are the
+    dequantised latent followed by the RoPE values, values the latent only."""
+    for dup in (0.0, 0.2):
+        wl = W.small(61, T=4, H=8, K=128, layout=ROPE, seq_len=96, page_size=16,
+                     dup_frac=dup, all_masked=(1,))
+        pool = build_pool(orc, wl)
+        out, lse, err = _run(orc, wl, pool)
+        assert err == 0
+        X = dequant_pool(pool, ROPE)
+        Xk = np.concatenate([X, rope_pool(pool)], axis=1)
+        ref, ref_lse = dense_attention(_qhat(wl), X, count_matrix(wl), wl.softmax_scale, Xk=Xk)
+        _close(out, ref)
+        _close(lse, ref_lse)
+
+
+def pin_attention_rope_zero_query_part(orc):
+    """A zero RoPE part of the query reduces a 656-byte row to the 528-byte
+    row before it: identical results (the RoPE terms are exact zeros)."""
+    wl = W.small(62, T=3, H=16, K=256, layout=ROPE, seq_len=300, page_size=16)
+    q = wl.q.copy()
+    q[:, :, 512:] = 0
+    wl = W.Workload(**{**wl.__dict__, "q": q})
+    pool = build_pool(orc, wl)
+    out, lse, _ = _run(orc, wl, pool)
+    wl528 = W.Workload(**{**wl.__dict__, "q": np.ascontiguousarray(q[:, :, :512]),
+                          "layout": SCALED})
+    out2, lse2, _ = _run(orc, wl528, np.ascontiguousarray(pool[:, :528]))
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def pin_attention_rope_only_scores(orc):
+    """Closed form: a zero latent part of the query leaves s_j = scale *
+    q_rope . k_rope; two live entries with RoPE parts e_0 and 2 e_0 give
+    weights in the ratio exp(scale * q_rope[0] * (1 - 2))."""
+    wl = W.small(63, T=1, H=8, K=128, layout=ROPE, seq_len=32, page_size=16, neg_frac=0.0)
+    topk = np.full((1, 128), -1, np.int32)
+    topk[0, 0], topk[0, 1] = 3, 9
+    q = np.zeros_like(wl.q)
+    q[0, :, 512] = W.bf16_bits(np.float32([1.5]))[0]
+    wl = W.Workload(**{**wl.__dict__, "topk": topk, "q": q})
+    pool = build_pool(orc, wl)
+    s0, s1 = [int(wl.page_table[0, i // 16]) * 16 + i % 16 for i in (3, 9)]
+    pool[[s0, s1], 528:656] = 0
+    pool[s0, 528:530] = W.bf16_bits(np.float32([1.0])).view(np.uint8)
+    pool[s1, 528:530] = W.bf16_bits(np.float32([2.0])).view(np.uint8)
+    out, lse, err = _run(orc, wl, pool)
+    X = dequant_pool(pool, ROPE)
+    a = wl.softmax_scale * 1.5
+    w0, w1 = 1.0, math.exp(a * (2.0 - 1.0))
+    want = (w0 * X[s0] + w1 * X[s1]) / (w0 + w1)
+    for h in range(8):
+        _close(out[0, h], want)
+        _close(np.array([lse[0, h]]), np.array([a * 1.0 + math.log(w0 + w1)]))
 
 
 def pin_attention_fp8_query(orc):

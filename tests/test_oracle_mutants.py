@@ -70,8 +70,13 @@ MUTANTS = [
     ("softmax_no_normalise", "o[d] /= L;", "o[d] /= 1.0;"),
     ("lse_log_dropped", "jb->lse[(int64_t)t * jb->H + h] = M + log(L);",
      "jb->lse[(int64_t)t * jb->H + h] = M;"),
-    ("query_head_ignored", "int64_t qoff = ((int64_t)t * jb->H + h) * ORC_D;",
-     "int64_t qoff = ((int64_t)t * jb->H + (h & ~1)) * ORC_D;"),
+    ("query_head_ignored", "int64_t qoff = ((int64_t)t * jb->H + h) * (ORC_D + rope);",
+     "int64_t qoff = ((int64_t)t * jb->H + (h & ~1)) * (ORC_D + rope);"),
+    ("rope_term_dropped", "dot += qh[ORC_D + r] * xr[(int64_t)j * ORC_ROPE + r];",
+     "dot += 0.0 * qh[ORC_D + r] * xr[(int64_t)j * ORC_ROPE + r];"),
+    ("rope_byte_order", "(row[ORC_SCALED_BYTES + 2 * r + 1] << 8)", "(row[ORC_SCALED_BYTES + 2 * r + 1] << 7)"),
+    ("writer_rope_not_copied", "dst[ORC_SCALED_BYTES + 2 * r] = (uint8_t)(src[ORC_D + r] & 0xff);",
+     "dst[ORC_SCALED_BYTES + 2 * r] = 0;"),
     ("query_fp8_scale_ignored", "(double)jb->q_scale;", "1.0;"),
     ("all_masked_nan", "if (nv == 0) {", "if (nv < 0) {"),
     ("all_masked_lse_zero", "jb->lse[(int64_t)t * jb->H + h] = -INFINITY;",

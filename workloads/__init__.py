@@ -6,7 +6,7 @@ of the method's arithmetic: no FP8 encoding, no index resolution through the
 page table, no softmax.  Pool bytes are produced elsewhere (by the oracle's
 writer for parity inputs, by the product writer for benchmark filler).
 
-The five named workloads follow the configurations the library is measured on
+The named workloads follow the configurations the library is measured on
 (sizes and distributions in each builder's docstring).  Every draw comes from
 ``numpy.random.Generator(PCG64)`` children spawned from the workload's seed in
 a fixed order: pool, pages, q, topk, extras.
@@ -20,8 +20,9 @@ from typing import Optional
 import numpy as np
 
 D = 512
-RAW, SCALED = 0, 1
-ROW_BYTES = {RAW: 512, SCALED: 528}
+RAW, SCALED, ROPE = 0, 1, 2
+ROW_BYTES = {RAW: 512, SCALED: 528, ROPE: 656}
+ROPE_DIM = 64            # bf16 RoPE values after the 528-byte part of a 656-byte row
 POISON = 0xFF  # FP8 S.1111.111 is NaN, and 0xFFFFFFFF is an fp32 NaN
 
 
@@ -61,9 +62,9 @@ class Workload:
     seq_lens: Optional[np.ndarray]    # int32 [B]
     token_seq: Optional[np.ndarray]   # int32 [T]; None = token t is sequence t
     topk: np.ndarray                  # int32 [T, K], -1 = padding
-    q: np.ndarray                     # uint16 bf16 bits [T, H, 512]
+    q: np.ndarray                     # uint16 bf16 bits [T, H, 512] (656-byte rows: 576)
     softmax_scale: float
-    kv_new: Optional[np.ndarray] = None        # uint16 bf16 bits [N, 512]
+    kv_new: Optional[np.ndarray] = None        # uint16 bf16 bits [N, 512] (or 576)
     slot_mapping: Optional[np.ndarray] = None  # int64 [N]
     q_fp8: bool = False               # query is quantised to FP8 before attention
     seed: int = 0
@@ -75,6 +76,10 @@ class Workload:
     @property
     def row_bytes(self) -> int:
         return ROW_BYTES[self.layout]
+
+    @property
+    def rope_dim(self) -> int:
+        return ROPE_DIM if self.layout == ROPE else 0
 
     def used_pages(self, seqs=None) -> np.ndarray:
         """Physical pages owned by the given sequences (all if None)."""
@@ -115,7 +120,7 @@ def _slots_of_positions(pt_row: np.ndarray, pos: np.ndarray, page_size: int):
 
 
 # --------------------------------------------------------------------------
-# The five named workloads
+# The named workloads
 # --------------------------------------------------------------------------
 
 def tiny_decode(seed: int = 1) -> Workload:
@@ -162,6 +167,18 @@ def decode_batch(seed: int = 2) -> Workload:
                     np.full(B, L, np.int32), None, topk,
                     normal_bf16(r_q, (T, H, D)), softmax_scale_512(),
                     kv_new, slot_mapping, seed=seed)
+
+
+def rope_decode(seed: int = 6) -> Workload:
+    """The decode batch's shape (64 sequences x 8192 tokens, page size 64, a
+    2^20-slot pool, H=16, top-k 2048 with 5% -1) over 656-byte RoPE rows
+    (group-scaled latent + 64 bf16 RoPE values) and 576-wide bf16 queries."""
+    wl = decode_batch(seed)
+    r_q, r_x = _streams(seed)[2], _streams(seed)[4]
+    return Workload("rope_decode", wl.T, wl.H, wl.K, ROPE, wl.page_size, wl.num_slots,
+                    wl.page_table, wl.seq_lens, None, wl.topk,
+                    normal_bf16(r_q, (wl.T, wl.H, D + ROPE_DIM)), softmax_scale_512(),
+                    normal_bf16(r_x, (wl.T, D + ROPE_DIM)), wl.slot_mapping, seed=seed)
 
 
 def scaled_decode(seed: int = 3) -> Workload:
@@ -262,6 +279,7 @@ NAMED = {
     "scaled_decode": scaled_decode,
     "q8_prefill": q8_prefill,
     "mixed_decode": mixed_decode,
+    "rope_decode": rope_decode,
 }
 
 
@@ -309,17 +327,22 @@ def small(seed: int, *, T: int = 5, H: int = 16, K: int = 256,
     return Workload(f"small{seed}", T, H, K, layout, page_size,
                     total_pages * page_size, None if physical else pt,
                     None if physical else np.full(B, seq_len, np.int32),
-                    token_seq, topk, normal_bf16(r_q, (T, H, D)),
+                    token_seq, topk,
+                    normal_bf16(r_q, (T, H, D + (ROPE_DIM if layout == ROPE else 0))),
                     softmax_scale_512(), seed=seed)
 
 
 def pool_content(seed: int, n_rows: int, layout: int):
     """Latents (uint16 bf16 bits [n_rows, 512], N(0,1)) for materialised pool
     rows, plus group scales ([n_rows, 4] fp32, 2**U(-6,2)) for the scaled
-    layout (None for raw).  The caller encodes the latents to FP8."""
+    and RoPE layouts (None for raw); RoPE layout: the latents carry 64 more
+    N(0,1) bf16 columns, the RoPE values.  The caller encodes the first 512
+    latent values to FP8."""
     r_pool = _streams(seed)[0]
     lat = normal_bf16(r_pool, (n_rows, D))
-    sc = log_uniform_scales(r_pool, n_rows) if layout == SCALED else None
+    sc = log_uniform_scales(r_pool, n_rows) if layout in (SCALED, ROPE) else None
+    if layout == ROPE:
+        lat = np.concatenate([lat, normal_bf16(r_pool, (n_rows, ROPE_DIM))], axis=1)
     return lat, sc
 
 
