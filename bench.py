@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_batch",
                     choices=["decode_batch", "scaled_decode", "mixed_decode",
-                             "q8_prefill", "tiny_decode"])
+                             "q8_prefill", "tiny_decode", "rope_decode"])
     ap.add_argument("--layers", type=int, default=0,
                     help="layer pools to rotate over (0 = enough for 1 GiB)")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "fp32"])
@@ -77,6 +77,7 @@ def main():
     if args.op == "transform":
         return bench_transform(args, wl, dev)
     T, H, K, R = wl.T, wl.H, wl.K, wl.row_bytes
+    rope = wl.rope_dim                                 # RoPE values per row (656-byte rows)
     prefill = wl.q_fp8
     phase = 1 if prefill else 0
     out_dtype = dsa.DSA_BF16 if args.out_dtype == "bf16" else dsa.DSA_FP32
@@ -112,13 +113,13 @@ def main():
         chunk = 1 << 18
         for i in range(0, used.numel(), chunk):
             sl_i = used[i:i + chunk]
-            lat = torch.randn((sl_i.numel(), 512), generator=gen, device=dev,
+            lat = torch.randn((sl_i.numel(), 512 + rope), generator=gen, device=dev,
                               dtype=torch.float32).to(torch.bfloat16)
-            dsa.check(dsa.dsa_kv_write(lat, sl_i.numel(), 512, dsa.DSA_BF16, 512, 0,
+            dsa.check(dsa.dsa_kv_write(lat, sl_i.numel(), 512 + rope, dsa.DSA_BF16, 512, rope,
                                        sl_i, pool, wl.num_slots, wl.layout,
                                        dsa.DSA_FP8_E4M3FN))
         pools.append(pool)
-        qs.append(torch.randn((T, H, 512), generator=gen, device=dev,
+        qs.append(torch.randn((T, H, 512 + rope), generator=gen, device=dev,
                               dtype=torch.float32).to(torch.bfloat16))
     torch.cuda.synchronize()
 
@@ -136,7 +137,7 @@ def main():
     def step(i, ev=None):
         layer = i % layers
         pool = pools[layer]
-        dsa.check(dsa.dsa_kv_write(kv_new, n_new, 512, dsa.DSA_BF16, 512, 0,
+        dsa.check(dsa.dsa_kv_write(kv_new, n_new, 512 + rope, dsa.DSA_BF16, 512, rope,
                                    slot_map, pool, wl.num_slots, wl.layout,
                                    dsa.DSA_FP8_E4M3FN))
         if prefill:
@@ -148,7 +149,7 @@ def main():
             q, qd, qsc = qs[layer], dsa.DSA_BF16, None
         if ev is not None:
             ev[0].record()
-        dsa.check(attn(q, qd, qsc, T, H, 512, 0, pool, wl.num_slots, wl.layout,
+        dsa.check(attn(q, qd, qsc, T, H, 512, rope, pool, wl.num_slots, wl.layout,
                        dsa.DSA_FP8_E4M3FN, topk, K, pt, wl.page_size, max_pages,
                        num_seqs, ts, sl, wl.softmax_scale, out, out_dtype, lse,
                        ws, wsb, None))
@@ -346,8 +347,10 @@ def cpu_baseline(wl, budget_s):
     pool = np.zeros((wl.num_slots, R), np.uint8)
     slots = wl.page_slots(wl.used_pages())
     pool[slots, :512] = W.random_fp8_codes(rng, (len(slots), 512))
-    if R == 528:
-        pool[slots, 512:] = W.log_uniform_scales(rng, len(slots)).view(np.uint8)
+    if R >= 528:
+        pool[slots, 512:528] = W.log_uniform_scales(rng, len(slots)).view(np.uint8)
+    if R == 656:
+        pool[slots, 528:] = W.normal_bf16(rng, (len(slots), 64)).view(np.uint8)
     sel = slice(0, T_s)
     q = wl.q[sel]
     q8 = scale = None

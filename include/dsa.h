@@ -18,6 +18,9 @@
  *     s_j = softmax_scale * q_scale * <q[t,h,:], x_j>
  *     out[t,h,:] = sum_j exp(s_j - m) x_j / sum_j exp(s_j - m)
  *     lse[t,h]   = m + log(sum_j exp(s_j - m))            (natural log)
+ * With 656-byte RoPE rows the query is 512 + 64 wide and the score adds the
+ * RoPE part: s_j += softmax_scale * <q[t,h,512:576], r_j> over the row's 64
+ * RoPE values r_j; the value (and out) stays the 512-wide latent.
  * A duplicated entry counts once per occurrence (no de-duplication [SCALED,
  * Modifications]).  A token with no valid entry gets out = 0 exactly and
  * lse = -inf (the pages leave this contract open [SCALED, Accuracy Tests]).
@@ -28,8 +31,10 @@
  *   DSA_KV_SCALED_FP8_528  512 E4M3FN codes, then four little-endian fp32
  *                          scales; scale g multiplies elements [128g,128g+128)
  *                          [SCALED, Motivation].
- *   DSA_KV_SCALED_FP8_656  the RoPE variant [SCALED, Motivation]; named only so
- *                          it can be rejected.
+ *   DSA_KV_SCALED_FP8_656  the RoPE variant the readers keep [SCALED,
+ *                          Motivation]; the pages give only its size.  Read
+ *                          here as the 528-byte row followed by 64
+ *                          little-endian bf16 RoPE values (bytes 528..655).
  * E4M3FNUZ is rejected before any launch [RAW, Modifications].
  *
  * Conventions for every entry point:
@@ -88,9 +93,9 @@ typedef enum dsa_status {
     DSA_ERR_LAUNCH = 9          /* the HIP runtime refused a launch           */
 } dsa_status;
 
-/* Bytes of one pool row for `layout`: 512 or 528; -1 for the 656-byte RoPE
- * layout and unknown values (not supported).  [RAW, Accuracy Tests: exported
- * buffer lengths are part of the tested surface.] */
+/* Bytes of one pool row for `layout`: 512, 528 or 656; -1 for unknown
+ * values.  [RAW, Accuracy Tests: exported buffer lengths are part of the
+ * tested surface.] */
 int32_t dsa_kv_row_bytes(int32_t layout);
 
 /* Static, NUL-terminated name of a status code ("DSA_OK", ...). */
@@ -103,11 +108,11 @@ const char *dsa_status_string(int32_t status);
  * the 528-byte rows].
  *
  *   kv            [n, kv_row_stride] elements of kv_dtype (DSA_BF16 only);
- *                 the first 512 of each row are written.  16-byte aligned,
- *                 kv_row_stride * 2 a multiple of 16.
+ *                 the first 512 of each row are written (656-byte layout:
+ *                 the first 576, the latent then the RoPE values).  16-byte
+ *                 aligned, kv_row_stride * 2 a multiple of 16.
  *   kv_dim        latent width of kv; must be 512 (DSA_ERR_WIDTH_MISMATCH).
- *   rope_dim      must be 0: the 656-byte RoPE rows are not supported
- *                 (DSA_ERR_LAYOUT).
+ *   rope_dim      64 for DSA_KV_SCALED_FP8_656, else 0 (DSA_ERR_LAYOUT).
  *   slot_mapping  [n] int64 physical slot of each row; a negative slot skips
  *                 the row; a slot >= num_slots skips it and is counted.
  *   pool          [num_slots, dsa_kv_row_bytes(layout)] bytes, 16-byte
@@ -115,7 +120,8 @@ const char *dsa_status_string(int32_t status);
  *   fp8_format    DSA_FP8_E4M3FN (FNUZ and others: DSA_ERR_DTYPE).
  * Encoding: round to nearest even, saturating to +-448, NaN kept as NaN.
  * Scaled rows: per 128-group s = fp32(amax / 448) (1 when amax = 0), codes
- * E4M3(fp32(x / s)), scales stored after the codes.  n == 0 is a no-op.
+ * E4M3(fp32(x / s)), scales stored after the codes; 656-byte rows then take
+ * the 64 RoPE values as bf16, unchanged.  n == 0 is a no-op.
  */
 int32_t dsa_kv_write(const void *kv, int64_t n, int64_t kv_row_stride,
                      int32_t kv_dtype, int32_t kv_dim, int32_t rope_dim,
@@ -153,11 +159,14 @@ size_t dsa_quantize_q_workspace_bytes(int64_t n_elems);
  * The FP8-query path reads q as E4M3FN codes times *q_scale [Q8, Motivation
  * and Modifications: FP8 query against FP8 KV].
  *
- *   q           [T, H, D] contiguous, q_dtype DSA_BF16 or DSA_FP8_E4M3FN;
- *               16-byte aligned.
+ *   q           [T, H, D + rope_dim] contiguous, q_dtype DSA_BF16 or
+ *               DSA_FP8_E4M3FN (656-byte rows: DSA_BF16 only, else
+ *               DSA_ERR_DTYPE -- the FP8 query path is NoPE-only [Q8,
+ *               Modifications]); 16-byte aligned.
  *   q_scale     one fp32 (device) for an FP8 query, else ignored (may be NULL).
- *   D           must be 512 (DSA_ERR_WIDTH_MISMATCH); rope_dim must be 0
- *               (DSA_ERR_LAYOUT).  1 <= H <= 128.  T == 0 is a no-op.
+ *   D           must be 512 (DSA_ERR_WIDTH_MISMATCH); rope_dim must be 64
+ *               for DSA_KV_SCALED_FP8_656 and 0 otherwise (DSA_ERR_LAYOUT).
+ *               1 <= H <= 128.  T == 0 is a no-op.
  *   pool        [num_slots, row bytes of `layout`], 16-byte aligned.
  *   topk        [T, K] int32; K a positive multiple of 128, at most 65536.
  *               Entry i: -1 is padding; other values are positions resolved

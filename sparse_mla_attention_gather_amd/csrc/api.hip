@@ -41,10 +41,14 @@ int32_t check_fp8_format(int32_t f) {
 }
 
 int32_t check_layout(int32_t layout) {
-    return (layout == DSA_KV_RAW_FP8_512 || layout == DSA_KV_SCALED_FP8_528)
+    return (layout == DSA_KV_RAW_FP8_512 || layout == DSA_KV_SCALED_FP8_528 ||
+            layout == DSA_KV_SCALED_FP8_656)
                ? DSA_OK
                : DSA_ERR_LAYOUT;
 }
+
+// The RoPE width a layout carries: 64 for the 656-byte rows, else 0.
+int32_t rope_of(int32_t layout) { return layout == DSA_KV_SCALED_FP8_656 ? 64 : 0; }
 
 // Shared validation of the two attention entry points.
 int32_t validate_attn(const void *q, int32_t q_dtype, const float *q_scale,
@@ -57,11 +61,13 @@ int32_t validate_attn(const void *q, int32_t q_dtype, const float *q_scale,
                       void *out, int32_t out_dtype, void *workspace,
                       size_t workspace_bytes, int32_t phase) {
     if (D != 512) return DSA_ERR_WIDTH_MISMATCH;
-    if (rope_dim != 0) return DSA_ERR_LAYOUT;
     int32_t st = check_layout(layout);
     if (st) return st;
+    if (rope_dim != rope_of(layout)) return DSA_ERR_LAYOUT;
     if ((st = check_fp8_format(fp8_format))) return st;
     if (q_dtype != DSA_BF16 && q_dtype != DSA_FP8_E4M3FN) return DSA_ERR_DTYPE;
+    // the FP8 query path is NoPE-only [Q8, Modifications]
+    if (rope_dim != 0 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
     if (out_dtype != DSA_BF16 && out_dtype != DSA_FP32) return DSA_ERR_DTYPE;
     if (T < 0 || H < 1 || H > 128) return DSA_ERR_SHAPE;
     if (K <= 0 || K % 128 != 0 || K > 65536) return DSA_ERR_SHAPE;
@@ -140,6 +146,7 @@ extern "C" {
 int32_t dsa_kv_row_bytes(int32_t layout) {
     if (layout == DSA_KV_RAW_FP8_512) return 512;
     if (layout == DSA_KV_SCALED_FP8_528) return 528;
+    if (layout == DSA_KV_SCALED_FP8_656) return 656;
     return -1;
 }
 
@@ -165,12 +172,12 @@ int32_t dsa_kv_write(const void *kv, int64_t n, int64_t kv_row_stride,
                      int64_t num_slots, int32_t layout, int32_t fp8_format,
                      int32_t *err_count, void *stream) {
     if (kv_dim != 512) return DSA_ERR_WIDTH_MISMATCH;
-    if (rope_dim != 0) return DSA_ERR_LAYOUT;
     int32_t st = check_layout(layout);
     if (st) return st;
+    if (rope_dim != rope_of(layout)) return DSA_ERR_LAYOUT;
     if ((st = check_fp8_format(fp8_format))) return st;
     if (kv_dtype != DSA_BF16) return DSA_ERR_DTYPE;
-    if (n < 0 || num_slots < 0 || kv_row_stride < 512) return DSA_ERR_SHAPE;
+    if (n < 0 || num_slots < 0 || kv_row_stride < 512 + rope_dim) return DSA_ERR_SHAPE;
     if (n > ((int64_t)1 << 33)) return DSA_ERR_SHAPE;
     if (n == 0) return DSA_OK;
     if (!kv || !slot_mapping || !pool) return DSA_ERR_NULL;

@@ -94,14 +94,18 @@ constexpr float kSlack = 8.0f;     // log2 headroom of a running max (P <= 256)
 // without a select, and far below any real score.
 constexpr float kNoMax = -1.0e30f;
 
-// LDS map (bytes) for NT head tiles of 16
-template <int NT>
+// LDS map (bytes) for NT head tiles of 16 and a row layout.  656-byte rows
+// add a ring of RoPE parts (64 rows x 128 B per tile) and, to stay within the
+// 160 KB of a CU, keep three tile buffers instead of four.
+template <int NT, int LAYOUT>
 struct Lds {
     static constexpr int kHB = 16 * NT;
+    static constexpr int kNB = LAYOUT == 2 ? 3 : kNBuf;          // tile buffers
     static constexpr int kParts = 2;                             // QK dim parts
     static constexpr int kBufBytes = kTile * 512;                // 32 KB payload
     static constexpr int kScBytes = kTile * 16;                  // 1 KB scales
-    static constexpr int kOffScales = kNBuf * kBufBytes;
+    static constexpr int kRopeTile = kTile * 2 * kRopeDim;       // 8 KB RoPE parts
+    static constexpr int kOffScales = kNB * kBufBytes;
     static constexpr int kOffSlots = kOffScales + kNScale * kScBytes;
     // partial S^T of the waves holding dim parts 1.. (16 x 16 fp32 each)
     static constexpr int kOffSp = kOffSlots + kMaxSplit * 4;
@@ -119,10 +123,12 @@ struct Lds {
     // per head and quarter: 1 when the quarter's maximum did not move this
     // tile (then it equals the reference maximum), two tiles (by parity)
     static constexpr int kOffFlags = kOffSmax + 2 * 16;
-    static constexpr int kBytes = kOffFlags + 2 * kHB * 4;
+    static constexpr int kOffRope = kOffFlags + 2 * kHB * 4;     // 16-byte aligned
+    static constexpr int kBytes = kOffRope + (LAYOUT == 2 ? kNB * kRopeTile : 0);
     // the token's page-table row is staged over the sp and P areas
     static constexpr int kPtPer = (kSpBytes + 2 * kPBytes) / 4 / kThreads;
     static_assert(kBytes <= 160 * 1024, "LDS budget");
+    static_assert(kOffRope % 16 == 0 && kOffScales % 16 == 0, "16-byte DMA destinations");
     static_assert(kPtPer >= 1, "page-table staging");
 };
 
@@ -130,7 +136,7 @@ struct Lds {
 // slot).  64 distinct zero rows, picked by the tile row, keep these reads off
 // a single set of L2 lines.
 constexpr int kZeroRows = 64;
-__device__ __attribute__((aligned(16))) const uint8_t kZeroRow[kZeroRows * kScaledBytes] = {};
+__device__ __attribute__((aligned(16))) const uint8_t kZeroRow[kZeroRows * kRopeRowBytes] = {};
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
@@ -221,7 +227,8 @@ __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_base) {
 // Slots of the rows this wave copies for one tile (see issue_tile).
 struct TileSlots {
     int32_t row[kLoadsRaw];
-    int32_t sc;
+    int32_t sc;     // the scale words' row (lanes 0-3)
+    int32_t rp;     // the RoPE part's row (lanes 0-31)
 };
 
 template <int LAYOUT>
@@ -230,7 +237,8 @@ __device__ __forceinline__ TileSlots read_slots(const int32_t *slots, int tile_b
     const int r0 = kRowsPerWave * w;
 #pragma unroll
     for (int k = 0; k < kLoadsRaw; k++) s.row[k] = slots[tile_base + r0 + 2 * k + (lane >> 5)];
-    s.sc = LAYOUT == 1 ? slots[tile_base + r0 + (lane & (kRowsPerWave - 1))] : 0;
+    s.sc = LAYOUT >= 1 ? slots[tile_base + r0 + (lane & (kRowsPerWave - 1))] : 0;
+    s.rp = LAYOUT == 2 ? slots[tile_base + r0 + ((lane >> 3) & (kRowsPerWave - 1))] : 0;
     return s;
 }
 
@@ -238,12 +246,14 @@ __device__ __forceinline__ TileSlots read_slots(const int32_t *slots, int tile_b
 // `sbuf`: wave w moves rows [4w, 4w+4), two rows per instruction (lane l ->
 // row 4w + 2k + (l >> 5), LDS chunk position l & 31, holding global chunk
 // (l & 31) ^ swz(row)); scaled rows add one 4-lane instruction for the rows'
-// 16-byte scale words.
+// 16-byte scale words; 656-byte rows one 32-lane instruction for their RoPE
+// parts (lane l -> row 4w + (l >> 3), position l & 7 of the row's 128 bytes
+// in ring slot `buf`, holding chunk (l & 7) ^ swz(row)).
 template <int LAYOUT, int NT>
 __device__ __forceinline__ void issue_tile(const AttnArgs &a, uint32_t lds0, const TileSlots &s,
                                            int buf, int sbuf, int w, int lane) {
-    using L = Lds<NT>;
-    constexpr int64_t kRow = LAYOUT == 0 ? kRawBytes : kScaledBytes;
+    using L = Lds<NT, LAYOUT>;
+    constexpr int64_t kRow = LAYOUT == 0 ? kRawBytes : LAYOUT == 1 ? kScaledBytes : kRopeRowBytes;
     const int r0 = kRowsPerWave * w;
     const uint32_t dst = lds0 + buf * L::kBufBytes + r0 * 512;
     const int pos = lane & 31;
@@ -255,7 +265,7 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, uint32_t lds0, con
                                            : kZeroRow + r * kRow + chunk * 16;
         dma16(src, dst + k * 1024);
     }
-    if (LAYOUT == 1) {
+    if (LAYOUT >= 1) {
         if (lane < kRowsPerWave) {
             const int r = r0 + lane;
             const uint8_t *src = s.sc >= 0 ? a.pool + (int64_t)s.sc * kRow + kD
@@ -263,11 +273,21 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, uint32_t lds0, con
             dma16(src, lds0 + L::kOffScales + sbuf * L::kScBytes + r0 * 16);
         }
     }
+    if (LAYOUT == 2) {
+        if (lane < 8 * kRowsPerWave) {
+            const int r = r0 + (lane >> 3);
+            const int chunk = (lane & 7) ^ swz(r);
+            const uint8_t *src = s.rp >= 0 ? a.pool + (int64_t)s.rp * kRow + kScaledBytes + chunk * 16
+                                           : kZeroRow + r * kRow + kScaledBytes + chunk * 16;
+            dma16(src, lds0 + L::kOffRope + buf * L::kRopeTile + r0 * 2 * kRopeDim);
+        }
+    }
 }
 
 template <int LAYOUT, bool QFP8, bool OUT_BF16, bool SPLIT, int NT>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
-    using L = Lds<NT>;
+    using L = Lds<NT, LAYOUT>;
+    constexpr int kNB = L::kNB;                  // tile buffers
     constexpr int kHB = L::kHB;
     constexpr int kParts = L::kParts;            // dim parts of the QK reduction
     constexpr int kDP = kD / kParts;             // dims per part: 128 or 256
@@ -288,14 +308,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     constexpr bool kPipe = true;
 #endif
     static_assert(kParts == 2, "one publishing wave per head tile and quarter");
-    constexpr bool kLate = kPipe && NT == 2;     // PV operands read in their own step
+    // PV operands read in their own step (one register set; a tile's buffer
+    // is refilled right after its step): 32-head blocks and 656-byte rows,
+    // whose extra operands would not fit otherwise
+    constexpr bool kLate = kPipe && (NT == 2 || LAYOUT == 2);
     constexpr int kDT = kPipe ? 4 : 2;           // PV: 16-dim tiles per wave
 #ifndef DSA_FILL0
 #define DSA_FILL0 2
 #endif
     constexpr int kFill0 = DSA_FILL0;            // tiles requested before the first lands
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    constexpr int kLoads = kLoadsRaw + (LAYOUT == 1 ? 1 : 0);
+    constexpr int kLoads = kLoadsRaw + (LAYOUT >= 1 ? 1 : 0) + (LAYOUT == 2 ? 1 : 0);
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
@@ -316,6 +339,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     //   sequential: wave w scores quarter w & 3 of head tile (w >> 2) /
     //     kParts, and the dp = 0 waves own it.
     constexpr bool kRowPair = kPipe && NT == 2 && !QFP8;
+    // scoring waves read a tile's row chunks in the tile's own step rather
+    // than during the softmax before (possible with kLate's buffer rotation)
+    constexpr bool kOwnStep = kRowPair || (kPipe && LAYOUT == 2);
     constexpr int kRT = kRowPair ? 2 : 1;        // entry quarters a scoring wave scores
     constexpr int kQT = kRowPair ? 1 : (kPipe ? NT : 1);   // head tiles it scores
     const int rh = w & 1;
@@ -352,15 +378,22 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // + (kk>>1)*4 + g)*16 + (kk&1)*8, so that a lane's steps 2m, 2m+1 use one
     // 16-byte chunk of the row; FP8: bq8[nt][k2] = q8[h][dp*kDP + k2*128 +
     // g*32 .. +32].  Heads beyond H read head 0 and are not stored.
+    // 656-byte rows: query rows of 512 + 64, and bqr = the RoPE part of head
+    // c, dims dp*32 + g*8 .. +8 (B operand of one bf16 MFMA step per part).
+    constexpr int kQRow = kD + (LAYOUT == 2 ? kRopeDim : 0);
     bf16x8 bq[QFP8 ? 1 : kQT][QFP8 ? 1 : kSteps];
     i32x8 bq8[QFP8 ? kQT : 1][QFP8 ? kSteps8 : 1];
+    bf16x8 bqr;
     float sscale = a.softmax_scale * kLog2e;
     if constexpr (QFP8) sscale *= *a.q_scale;
     if (!is_v) {
 #pragma unroll
         for (int nt = 0; nt < kQT; nt++) {
             const int h = hb * kHB + ((kPipe && !kRowPair) ? nt : ht) * 16 + c;
-            const int64_t qrow = ((int64_t)t * a.H + (h < a.H ? h : 0)) * kD;
+            const int64_t qrow = ((int64_t)t * a.H + (h < a.H ? h : 0)) * kQRow;
+            if constexpr (LAYOUT == 2)
+                bqr = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+                    reinterpret_cast<const __bf16 *>(a.q) + qrow + kD + dp * 32 + g * 8));
             if constexpr (QFP8) {
                 const uint8_t *qp = reinterpret_cast<const uint8_t *>(a.q) + qrow + dp * kDP + g * 32;
 #pragma unroll
@@ -469,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                                    i, w, lane);
     auto fill_rest = [&]() {
 #pragma unroll
-        for (int i = kFill0; i < kNBuf; i++)
+        for (int i = kFill0; i < kNB; i++)
             if (i < n_tiles)
                 issue_tile<LAYOUT, NT>(a, lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
                                        i, w, lane);
@@ -492,6 +525,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // being scored, the PV transpose reads (tv) of the last two tiles (by
     // tile parity; one set when not pipelined or with kLate).
     u32x4 xc[kRT][kXc];
+    u32x4 xcr;                  // 656-byte rows: this lane's RoPE chunk
     u32x2 tv[kPipe && !kLate ? 2 : 1][2][kDT];
     f32x4 part[kRT * kQT];      // [entry quarter][head tile]
 
@@ -512,13 +546,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int rt = 0; rt < kRT; rt++) {
             const int r = 16 * (kRowPair ? 2 * rh + rt : wq) + c;
-            const uint8_t *xr = lds + (j % kNBuf) * L::kBufBytes + r * 512;
+            const uint8_t *xr = lds + (j % kNB) * L::kBufBytes + r * 512;
             const int sw = swz(r);
 #pragma unroll
             for (int m = 0; m < kXc; m++) {
                 const int ch = QFP8 ? dp * kChunks + (m >> 1) * 8 + g * 2 + (m & 1)
                                     : dp * kChunks + m * 4 + g;
                 xc[rt][m] = *reinterpret_cast<const u32x4 *>(xr + ((ch ^ sw) * 16));
+            }
+            if constexpr (LAYOUT == 2) {
+                // RoPE dims dp*32 + g*8 .. +8 of the same row: chunk dp*4 + g
+                const uint8_t *rr = lds + L::kOffRope + (j % kNB) * L::kRopeTile + r * (2 * kRopeDim);
+                xcr = *reinterpret_cast<const u32x4 *>(rr + (((dp * 4 + g) ^ sw) * 16));
             }
         }
     };
@@ -527,7 +566,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // dbase + 16dt ..
     auto read_tv = [&](int j, auto par) {
         constexpr int PAR = decltype(par)::value;
-        const uint8_t *xb = lds + (j % kNBuf) * L::kBufBytes;
+        const uint8_t *xb = lds + (j % kNB) * L::kBufBytes;
 #pragma unroll
         for (int ks = 0; ks < 2; ks++) {
             const int row = ks * 32 + g * 8 + (c >> 1);
@@ -548,7 +587,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     auto qk = [&](int j) {
         const float *scf = reinterpret_cast<const float *>(lds + L::kOffScales + (j % kNScale) * L::kScBytes);
         float scv[4][kGpp];
-        if constexpr (LAYOUT == 1) {
+        if constexpr (LAYOUT >= 1) {
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -618,6 +657,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                             part[rt * kQT + nt][i] = ag[0][i] * scv[i][0] + ag[1][i] * scv[i][kGpp - 1];
                         }
                     }
+            if constexpr (LAYOUT == 2) {
+                // this part's 32 RoPE dims: exact bf16 products, no scale
+                const f32x4 accr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, xcr), bqr, f32x4{0, 0, 0, 0}, 0, 0, 0);
+                part[0] += accr;
+            }
         }
         // publish every partial this wave does not own
 #pragma unroll
@@ -659,7 +704,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         const f32x4 mp = *reinterpret_cast<const f32x4 *>(
             lds + L::kOffMq + (par ^ 1) * L::kMqBytes + hh * 16);
         float sc_own = 0.0f;
-        if constexpr (LAYOUT == 1)
+        if constexpr (LAYOUT >= 1)
             sc_own = reinterpret_cast<const float *>(lds + L::kOffScales + (j % kNScale) * L::kScBytes)[lane * 4 + wq];
         then();
         const int slv[4] = {sl4.x, sl4.y, sl4.z, sl4.w};
@@ -697,7 +742,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         const u32x2 pk = {__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
         *reinterpret_cast<u32x2 *>(p_w + p_off(hh, 2 * wq + (g >> 1)) + (g & 1) * 8) = pk;
         if (g == 0) mq_w[hh * 4 + wq] = m_own;
-        if constexpr (LAYOUT == 1) {
+        if constexpr (LAYOUT >= 1) {
             // largest scale of group wq over the tile's 64 entries
             const float smax = max_over_g(dpp_max16(sc_own));
             if (lane == 0) reinterpret_cast<float *>(lds + L::kOffSmax)[par * 4 + wq] = smax;
@@ -766,7 +811,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             }
         }
         float smax = 1.0f;
-        if constexpr (LAYOUT == 1) {
+        if constexpr (LAYOUT >= 1) {
             // scale group dbase/128 of each entry, normalised by the tile's
             // largest (published with P) so that the f16 operand stays in
             // range; the factor is put back when the tile's product is added
@@ -908,11 +953,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         // step k itself, into a single register set, and tile k's buffer
         // (not tile k+1's) takes the next tile after step k, so that kNBuf - 1
         // tiles rather than kNBuf are in flight beyond the one being scored.
-        constexpr int kAhead = kLate ? kNBuf - 1 : kNBuf;
+        constexpr int kAhead = kLate ? kNB - 1 : kNB;
         auto refill = [&](int k, const TileSlots &nsl) {
             const int nx = k + 1 + kAhead;
             if (nx < n_tiles)
-                issue_tile<LAYOUT, NT>(a, lds0, nsl, nx % kNBuf, nx % kNScale, w, lane);
+                issue_tile<LAYOUT, NT>(a, lds0, nsl, nx % kNB, nx % kNScale, w, lane);
         };
         // tile 0's operands, then (16 heads) its buffer takes tile kNBuf
         // (each role keeps its own registers: nothing flows from one role's
@@ -922,10 +967,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             barrier_raw();
             fill_rest();
             read_ops();
-            const TileSlots nsl = read_slots<LAYOUT>(slots, min(kNBuf, n_tiles - 1) * kTile, w, lane);
+            const TileSlots nsl = read_slots<LAYOUT>(slots, min(kNB, n_tiles - 1) * kTile, w, lane);
             wait_lgkm0();
             barrier_raw();
-            if (!kLate && kNBuf < n_tiles) issue_tile<LAYOUT, NT>(a, lds0, nsl, 0, kNBuf % kNScale, w, lane);
+            if (!kLate && kNB < n_tiles) issue_tile<LAYOUT, NT>(a, lds0, nsl, 0, kNB % kNScale, w, lane);
         };
         // (the role test goes through readfirstlane so that the compiler
         // sees a uniform branch and gives each role its own registers)
@@ -962,17 +1007,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             }
             epilogue(std::false_type{});
         } else {
-            // (kRowPair: a tile's row chunks are read in its own step, not
+            // (kOwnStep: a tile's row chunks are read in its own step, not
             // prefetched during the softmax before, so that they are not live
-            // beside the softmax; the tile's buffer outlives the step)
-            first_tile([&] { if constexpr (!kRowPair) read_xc(0); });
+            // beside the softmax; with kLate the tile's buffer outlives the
+            // step)
+            first_tile([&] { if constexpr (!kOwnStep) read_xc(0); });
             for (int k = 0; k < n_tiles; k++) {
                 const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + 1 + kAhead, n_tiles - 1) * kTile, w, lane);
-                if constexpr (kRowPair) read_xc(k);
+                if constexpr (kOwnStep) read_xc(k);
                 qk(k);
                 wait_tile(k + 1, k + kAhead);
                 barrier_raw();
-                const bool pre = !kRowPair && k + 1 < n_tiles;
+                const bool pre = !kOwnStep && k + 1 < n_tiles;
                 if (owner) softmax(k, [&] { if (pre) read_xc(k + 1); });
                 else if (pre) read_xc(k + 1);
                 wait_lgkm0();
@@ -986,9 +1032,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         // parity, so the owners can read the previous tile's maxima while
         // they publish the current ones
         for (int k = 0; k < n_tiles; k++) {
-            const bool refill = k + kNBuf < n_tiles;
-            const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + kNBuf, n_tiles - 1) * kTile, w, lane);
-            wait_tile(k, k == 0 ? kFill0 - 1 : k + kNBuf - 1);
+            const bool refill = k + kNB < n_tiles;
+            const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + kNB, n_tiles - 1) * kTile, w, lane);
+            wait_tile(k, k == 0 ? kFill0 - 1 : k + kNB - 1);
             barrier_raw();
             if (k == 0) fill_rest();
             read_xc(k);
@@ -998,7 +1044,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             // registers: the buffer takes the tile kNBuf ahead
             wait_lgkm0();
             barrier_raw();
-            if (refill) issue_tile<LAYOUT, NT>(a, lds0, nsl, k % kNBuf, (k + kNBuf) % kNScale, w, lane);
+            if (refill) issue_tile<LAYOUT, NT>(a, lds0, nsl, k % kNB, (k + kNB) % kNScale, w, lane);
             if (owner) softmax(k, nothing);
             wait_lgkm0();
             barrier_raw();
@@ -1150,7 +1196,7 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
     constexpr int kHB = 16 * NT;
     const int n_hb = (a.H + kHB - 1) / kHB;
     const dim3 grid((unsigned)(((int64_t)a.T + 7) / 8 * 8 * n_hb * a.n_splits));
-    constexpr int bytes = Lds<NT>::kBytes;
+    constexpr int bytes = Lds<NT, LAYOUT>::kBytes;
     if (a.n_splits > 1) {
         constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, true, NT>;
         allow_big_lds<kern>(bytes);
@@ -1187,6 +1233,8 @@ hipError_t launch_attn(const AttnArgs &a_in, int layout, bool q_fp8, bool out_bf
     DSA_DISPATCH(1, false, true)
     DSA_DISPATCH(1, true, false)
     DSA_DISPATCH(1, true, true)
+    DSA_DISPATCH(2, false, false)
+    DSA_DISPATCH(2, false, true)
 #undef DSA_DISPATCH
     return hipErrorInvalidValue;
 }

@@ -23,6 +23,10 @@ constexpr int kD = 512;          // latent width (kv_lora_rank)
 constexpr int kGroup = 128;      // elements per scale group (528-byte rows)
 constexpr int kRawBytes = 512;
 constexpr int kScaledBytes = 528;
+// 656-byte RoPE rows: the 528-byte scaled row, then 64 little-endian bf16
+// RoPE values (the pages give only the size; this split is the reading)
+constexpr int kRopeDim = 64;
+constexpr int kRopeRowBytes = 656;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
     return __uint_as_float(h16 << 16);

@@ -4,7 +4,9 @@
 // pool slot, for the raw 512-byte and the group-scaled 528-byte layouts
 // ("extend CUDA TileLang raw FP8 KV path", Modifications; "[DSA] Support
 // group-scaled FP8 NoPE KV reads for CUDA TileLang", Motivation: 512 FP8
-// values followed by four fp32 scales, one per 128 values).
+// values followed by four fp32 scales, one per 128 values), and the 656-byte
+// RoPE layout the same page says the readers keep (the scaled row followed by
+// the row's 64 RoPE values, copied as bf16).
 //
 // Mapping: one 64-lane wavefront per row; lane l owns elements [8l, 8l+8)
 // (one 16-byte load of bf16, one 8-byte store of codes), so a 128-element
@@ -36,7 +38,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
         x[2 * i] = bf16_bits_to_f32(raw[i] & 0xffffu);
         x[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
     }
-    constexpr int64_t kRow = LAYOUT == 0 ? kRawBytes : kScaledBytes;
+    constexpr int64_t kRow = LAYOUT == 0 ? kRawBytes : LAYOUT == 1 ? kScaledBytes : kRopeRowBytes;
     uint8_t *dst = pool + slot * kRow;
     if (LAYOUT == 0) {
         u32x2 codes = {pack4_e4m3(x[0], x[1], x[2], x[3]),
@@ -58,6 +60,11 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
         *reinterpret_cast<u32x2 *>(dst + lane * 8) = codes;
         if ((lane & 15) == 0)
             *reinterpret_cast<float *>(dst + kD + 4 * (lane >> 4)) = scale;
+        if (LAYOUT == 2 && lane < kRopeDim / 8) {
+            // the RoPE values after the latent: 16 bytes per lane
+            const u32x4 r = *reinterpret_cast<const u32x4 *>(kv + row * row_stride + kD + lane * 8);
+            *reinterpret_cast<u32x4 *>(dst + kScaledBytes + lane * 16) = r;
+        }
     }
 }
 
@@ -69,8 +76,11 @@ hipError_t launch_kv_write(const uint16_t *kv, int64_t n, int64_t row_stride,
     if (layout == 0)
         kv_write_kernel<0><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
             kv, n, row_stride, slot_mapping, pool, num_slots, err_count);
-    else
+    else if (layout == 1)
         kv_write_kernel<1><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+            kv, n, row_stride, slot_mapping, pool, num_slots, err_count);
+    else
+        kv_write_kernel<2><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
             kv, n, row_stride, slot_mapping, pool, num_slots, err_count);
     return hipGetLastError();
 }

@@ -68,7 +68,7 @@ def run_attn(di: DevInputs, pool_dev: torch.Tensor, *, phase: int = 0,
     fn = dsa.dsa_sparse_attn_decode if phase == 0 else dsa.dsa_sparse_attn_prefill
     fp8q = q_scale is not None
     check(fn(di.q if q is None else q, dsa.DSA_FP8_E4M3FN if fp8q else dsa.DSA_BF16,
-             q_scale, T, H, 512, 0, pool_dev, pool_dev.shape[0], wl.layout,
+             q_scale, T, H, 512, wl.rope_dim, pool_dev, pool_dev.shape[0], wl.layout,
              dsa.DSA_FP8_E4M3FN, di.topk if topk is None else topk, K,
              di.page_table, wl.page_size, di.max_pages, di.num_seqs,
              di.token_seq, di.seq_lens, wl.softmax_scale, out, out_dtype,
@@ -83,7 +83,8 @@ def run_kv_write(kv: np.ndarray, slot_mapping: np.ndarray, pool_dev: torch.Tenso
     kv_d = dev(kv)
     sm = dev(slot_mapping.astype(np.int64))
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    check(dsa.dsa_kv_write(kv_d, kv.shape[0], kv.shape[1], dsa.DSA_BF16, 512, 0,
+    check(dsa.dsa_kv_write(kv_d, kv.shape[0], kv.shape[1], dsa.DSA_BF16, 512,
+                           64 if layout == W.ROPE else 0,
                            sm, pool_dev, pool_dev.shape[0], layout,
                            dsa.DSA_FP8_E4M3FN, err))
     torch.cuda.synchronize()

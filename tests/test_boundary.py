@@ -48,7 +48,7 @@ def test_row_bytes_match_the_pages():
             rows[line[0]] = int(line[1])
     assert dsa.dsa_kv_row_bytes(dsa.DSA_KV_RAW_FP8_512) == rows["raw_fp8_nope"]
     assert dsa.dsa_kv_row_bytes(dsa.DSA_KV_SCALED_FP8_528) == rows["scaled_fp8_nope"]
-    assert dsa.dsa_kv_row_bytes(dsa.DSA_KV_SCALED_FP8_656) == -1
+    assert dsa.dsa_kv_row_bytes(dsa.DSA_KV_SCALED_FP8_656) == rows["scaled_fp8_rope"]
     assert dsa.dsa_kv_row_bytes(7) == -1
     assert rows["topk_multiple"] == 128
 
@@ -104,7 +104,10 @@ REJECT = [
     (dict(D=576), "DSA_ERR_WIDTH_MISMATCH"),
     (dict(D=256), "DSA_ERR_WIDTH_MISMATCH"),
     (dict(rope_dim=64), "DSA_ERR_LAYOUT"),
-    (dict(layout=dsa.DSA_KV_SCALED_FP8_656), "DSA_ERR_LAYOUT"),
+    (dict(layout=dsa.DSA_KV_SCALED_FP8_656), "DSA_ERR_LAYOUT"),        # rope_dim 0
+    (dict(layout=dsa.DSA_KV_SCALED_FP8_656, rope_dim=32), "DSA_ERR_LAYOUT"),
+    (dict(layout=dsa.DSA_KV_SCALED_FP8_656, rope_dim=64, q_dtype=dsa.DSA_FP8_E4M3FN,
+          q_scale=FAKE), "DSA_ERR_DTYPE"),                               # NoPE-only FP8 query
     (dict(layout=9), "DSA_ERR_LAYOUT"),
     (dict(fp8_format=dsa.DSA_FP8_E4M3FNUZ), "DSA_ERR_DTYPE"),
     (dict(fp8_format=dsa.DSA_BF16), "DSA_ERR_DTYPE"),
@@ -187,7 +190,8 @@ def kv_args(**over):
 KV_REJECT = [
     (dict(kv_dim=576), "DSA_ERR_WIDTH_MISMATCH"),
     (dict(rope_dim=64), "DSA_ERR_LAYOUT"),
-    (dict(layout=dsa.DSA_KV_SCALED_FP8_656), "DSA_ERR_LAYOUT"),
+    (dict(layout=dsa.DSA_KV_SCALED_FP8_656), "DSA_ERR_LAYOUT"),        # rope_dim 0
+    (dict(layout=dsa.DSA_KV_SCALED_FP8_656, rope_dim=64, kv_row_stride=512), "DSA_ERR_SHAPE"),
     (dict(fp8_format=dsa.DSA_FP8_E4M3FNUZ), "DSA_ERR_DTYPE"),
     (dict(kv_dtype=dsa.DSA_FP32), "DSA_ERR_DTYPE"),
     (dict(n=-1), "DSA_ERR_SHAPE"),
@@ -289,3 +293,15 @@ def test_build_rejects_kernels_that_use_scratch():
     assert B.scratch_users(ok) == []
     assert B.scratch_users(ok + bad) == [("k_bad", "VGPRs Spill", 3),
                                          ("k_bad", "ScratchSize [bytes/lane]", 16)]
+
+
+def test_rope_layout_passes_validation():
+    """656-byte rows with rope_dim 64 and a bf16 query (attention), or
+    576-wide input rows (writer), pass every argument check: the calls stop
+    at the device check (no GPU in this container)."""
+    for phase in (0, 1):
+        st = call(phase, layout=dsa.DSA_KV_SCALED_FP8_656, rope_dim=64)
+        assert st in (dsa.DSA_ERR_DEVICE, dsa.DSA_OK), dsa.dsa_status_string(st)
+    st = dsa.dsa_kv_write(**kv_args(layout=dsa.DSA_KV_SCALED_FP8_656, rope_dim=64,
+                                    kv_row_stride=576))
+    assert st in (dsa.DSA_ERR_DEVICE, dsa.DSA_OK), dsa.dsa_status_string(st)

@@ -35,9 +35,11 @@ def _materialise(orc, wl, seqs):
         host[slots] = tmp
     else:
         tmp = np.zeros((len(slots), 512), np.uint8)
-        orc.kv_write(lat, np.arange(len(slots)), tmp, W.RAW)
+        orc.kv_write(lat[:, :512], np.arange(len(slots)), tmp, W.RAW)
         host[slots, :512] = tmp
-        host[slots, 512:] = sc.view(np.uint8).reshape(len(slots), 16)
+        host[slots, 512:528] = sc.view(np.uint8).reshape(len(slots), 16)
+        if wl.layout == W.ROPE:
+            host[slots, 528:] = np.ascontiguousarray(lat[:, 512:]).view(np.uint8)
     pool = torch.full((wl.num_slots, R), W.POISON, dtype=torch.uint8, device=G.DEV)
     used = torch.from_numpy(wl.page_slots(wl.used_pages())).to(G.DEV)
     gen = torch.Generator(device=G.DEV)
@@ -49,9 +51,12 @@ def _materialise(orc, wl, seqs):
                           dtype=torch.int32)
         rows = torch.empty((u.numel(), R), dtype=torch.uint8, device=G.DEV)
         rows[:, :512] = (r + (r >= 0x7F).int()).to(torch.uint8)
-        if R == 528:
+        if R >= 528:
             s = torch.exp2(torch.rand((u.numel(), 4), generator=gen, device=G.DEV) * 8 - 6)
-            rows[:, 512:] = s.contiguous().view(torch.uint8)
+            rows[:, 512:528] = s.contiguous().view(torch.uint8)
+        if R == 656:
+            rp = torch.randn((u.numel(), 64), generator=gen, device=G.DEV).to(torch.bfloat16)
+            rows[:, 528:] = rp.contiguous().view(torch.uint8)
         pool[u] = rows
     pool[torch.from_numpy(slots).to(G.DEV)] = torch.from_numpy(host[slots]).to(G.DEV)
     return host, pool
@@ -110,6 +115,12 @@ def _decode_case(orc, wl, sample):
 def test_decode_batch_full(orc):
     wl = W.decode_batch()
     _decode_case(orc, wl, [0, 9, 31, 40, 63])
+
+
+def test_rope_decode_full(orc):
+    """The decode batch's shape over 656-byte RoPE rows."""
+    wl = W.rope_decode()
+    _decode_case(orc, wl, [0, 13, 32, 63])
 
 
 def test_scaled_decode_full(orc):

@@ -184,7 +184,7 @@ def test_attention_small(orc, cfg, phase, qfp8, od):
 
 
 @pytest.mark.parametrize("H", [16, 32])
-@pytest.mark.parametrize("layout", [W.RAW, W.SCALED], ids=["raw", "scaled"])
+@pytest.mark.parametrize("layout", [W.RAW, W.SCALED, W.ROPE], ids=["raw", "scaled", "rope"])
 @pytest.mark.parametrize("phase", [0, 1], ids=["decode", "prefill"])
 def test_trailing_masked_entries(orc, layout, phase, H):
     """Rows whose valid entries end early (every later entry -1, as ragged
@@ -209,6 +209,51 @@ def test_trailing_masked_entries(orc, layout, phase, H):
     for t in range(T):
         if widths[t % len(widths)] == 0:
             assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
+
+
+ROPE_SMALL = [
+    dict(seed=221, T=5, H=16, K=256, layout=W.ROPE),
+    dict(seed=222, T=3, H=8, K=384, layout=W.ROPE, dup_frac=0.2, neg_frac=0.3),
+    dict(seed=223, T=40, H=32, K=1664, layout=W.ROPE, seq_len=2000, page_size=64),
+    dict(seed=224, T=4, H=16, K=1024, layout=W.ROPE, seq_len=1500, page_size=64,
+         physical=True, all_masked=(2,)),
+]
+
+
+@pytest.mark.parametrize("cfg", ROPE_SMALL, ids=[f"s{c['seed']}" for c in ROPE_SMALL])
+@pytest.mark.parametrize("phase", [0, 1], ids=["decode", "prefill"])
+@pytest.mark.parametrize("od", [dsa.DSA_FP32, dsa.DSA_BF16], ids=["f32", "bf16"])
+def test_attention_rope_small(orc, cfg, phase, od):
+    """656-byte RoPE rows (bf16 query of 512 + 64): the writer's bytes and
+    the attention against the oracle."""
+    wl = W.small(**cfg)
+    pool = P.build_pool(orc, wl)
+    ref, ref_lse, ref_err = _oracle_attn(orc, wl, pool)
+    out, lse, err = G.run_attn(G.DevInputs(wl), G.dev(pool), phase=phase, out_dtype=od)
+    assert err == ref_err
+    G.assert_attn_close(out, ref, od, where=str(cfg))
+    G.assert_lse_close(lse, ref_lse, where=str(cfg))
+    for t in cfg.get("all_masked", ()):
+        assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
+
+
+def test_writer_rope_rows(orc):
+    """The writer on 656-byte rows, bit for bit: latent as the scaled rows,
+    then the 64 RoPE values; rows read with a stride wider than 576."""
+    rng = np.random.default_rng(17)
+    n, stride = 300, 640
+    kv = W.normal_bf16(rng, (n, stride))
+    kv[:7] = W.bf16_bits(np.float32(rng.standard_normal((7, stride)) * 1e4))
+    kv[9, :512] = 0
+    slots = rng.permutation(400)[:n].astype(np.int64)
+    slots[::17] = -1
+    ref = np.full((400, 656), 0x5A, np.uint8)
+    assert orc.kv_write(kv, slots, ref, W.ROPE) == 0
+    pool = torch.full((400, 656), 0x5A, dtype=torch.uint8, device=G.DEV)
+    assert G.run_kv_write(kv, slots, pool, W.ROPE) == 0
+    got = G.host(pool)
+    bad = np.nonzero(got != ref)
+    assert len(bad[0]) == 0, (len(bad[0]), bad[0][:4], bad[1][:4])
 
 
 def test_invalid_indices_are_masked_and_counted(orc):
