@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_batch",
                     choices=["decode_batch", "scaled_decode", "mixed_decode",
-                             "q8_prefill", "tiny_decode", "rope_decode"])
+                             "q8_prefill", "tiny_decode", "rope_decode", "bf16_decode"])
     ap.add_argument("--layers", type=int, default=0,
                     help="layer pools to rotate over (0 = enough for 1 GiB)")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "fp32"])
@@ -347,10 +347,12 @@ def cpu_baseline(wl, budget_s):
     pool = np.zeros((wl.num_slots, R), np.uint8)
     slots = wl.page_slots(wl.used_pages())
     pool[slots, :512] = W.random_fp8_codes(rng, (len(slots), 512))
-    if R >= 528:
+    if R in (528, 656):
         pool[slots, 512:528] = W.log_uniform_scales(rng, len(slots)).view(np.uint8)
     if R == 656:
         pool[slots, 528:] = W.normal_bf16(rng, (len(slots), 64)).view(np.uint8)
+    if R == 1024:
+        pool[slots] = W.normal_bf16(rng, (len(slots), 512)).view(np.uint8)
     sel = slice(0, T_s)
     q = wl.q[sel]
     q8 = scale = None

@@ -35,6 +35,9 @@
  *                          Motivation]; the pages give only its size.  Read
  *                          here as the 528-byte row followed by 64
  *                          little-endian bf16 RoPE values (bytes 528..655).
+ *   DSA_KV_BF16_1024       the 512 latent values as little-endian bf16, no
+ *                          cast: the pool the FP8 rows halve [RAW, Speed
+ *                          Tests: 512 B against 1024 B].  bf16 queries only.
  * E4M3FNUZ is rejected before any launch [RAW, Modifications].
  *
  * Conventions for every entry point:
@@ -69,7 +72,8 @@ extern "C" {
 typedef enum dsa_kv_layout {
     DSA_KV_RAW_FP8_512 = 0,
     DSA_KV_SCALED_FP8_528 = 1,
-    DSA_KV_SCALED_FP8_656 = 2
+    DSA_KV_SCALED_FP8_656 = 2,
+    DSA_KV_BF16_1024 = 3
 } dsa_kv_layout;
 
 typedef enum dsa_dtype {
@@ -93,7 +97,7 @@ typedef enum dsa_status {
     DSA_ERR_LAUNCH = 9          /* the HIP runtime refused a launch           */
 } dsa_status;
 
-/* Bytes of one pool row for `layout`: 512, 528 or 656; -1 for unknown
+/* Bytes of one pool row for `layout`: 512, 528, 656 or 1024; -1 for unknown
  * values.  [RAW, Accuracy Tests: exported buffer lengths are part of the
  * tested surface.] */
 int32_t dsa_kv_row_bytes(int32_t layout);
@@ -113,6 +117,8 @@ const char *dsa_status_string(int32_t status);
  *                 aligned, kv_row_stride * 2 a multiple of 16.
  *   kv_dim        latent width of kv; must be 512 (DSA_ERR_WIDTH_MISMATCH).
  *   rope_dim      64 for DSA_KV_SCALED_FP8_656, else 0 (DSA_ERR_LAYOUT).
+ *   fp8_format    DSA_FP8_E4M3FN for every layout (DSA_KV_BF16_1024 stores
+ *                 no FP8 but the argument is checked the same way).
  *   slot_mapping  [n] int64 physical slot of each row; a negative slot skips
  *                 the row; a slot >= num_slots skips it and is counted.
  *   pool          [num_slots, dsa_kv_row_bytes(layout)] bytes, 16-byte
@@ -121,7 +127,8 @@ const char *dsa_status_string(int32_t status);
  * Encoding: round to nearest even, saturating to +-448, NaN kept as NaN.
  * Scaled rows: per 128-group s = fp32(amax / 448) (1 when amax = 0), codes
  * E4M3(fp32(x / s)), scales stored after the codes; 656-byte rows then take
- * the 64 RoPE values as bf16, unchanged.  n == 0 is a no-op.
+ * the 64 RoPE values as bf16, unchanged.  DSA_KV_BF16_1024 rows are the
+ * input's 512 bf16 values, unchanged.  n == 0 is a no-op.
  */
 int32_t dsa_kv_write(const void *kv, int64_t n, int64_t kv_row_stride,
                      int32_t kv_dtype, int32_t kv_dim, int32_t rope_dim,
@@ -162,7 +169,7 @@ size_t dsa_quantize_q_workspace_bytes(int64_t n_elems);
  *   q           [T, H, D + rope_dim] contiguous, q_dtype DSA_BF16 or
  *               DSA_FP8_E4M3FN (656-byte rows: DSA_BF16 only, else
  *               DSA_ERR_DTYPE -- the FP8 query path is NoPE-only [Q8,
- *               Modifications]); 16-byte aligned.
+ *               Modifications]; bf16 rows: DSA_BF16 only); 16-byte aligned.
  *   q_scale     one fp32 (device) for an FP8 query, else ignored (may be NULL).
  *   D           must be 512 (DSA_ERR_WIDTH_MISMATCH); rope_dim must be 64
  *               for DSA_KV_SCALED_FP8_656 and 0 otherwise (DSA_ERR_LAYOUT).

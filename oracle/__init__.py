@@ -21,8 +21,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-RAW, SCALED, ROPE = 0, 1, 2
-ROW_BYTES = {RAW: 512, SCALED: 528, ROPE: 656}
+RAW, SCALED, ROPE, BF16 = 0, 1, 2, 3
+ROW_BYTES = {RAW: 512, SCALED: 528, ROPE: 656, BF16: 1024}
 ROPE_DIM = 64
 
 

@@ -38,6 +38,9 @@
 /* then 512 + 64 wide and the RoPE part adds q_rope . k_rope to the score.  */
 #define ORC_ROPE 64
 #define ORC_ROPE_BYTES 656
+/* BF16 row: the 512 latent values as bf16, 1024 bytes [RAW, Speed Tests and */
+/* Profiling: the BF16 pool the FP8 rows are compared against].              */
+#define ORC_BF16_BYTES 1024
 
 /* ------------------------------------------------------------------------ */
 /* FP8 E4M3FN (OCP): sign | 4 exponent bits (bias 7) | 3 mantissa bits.      */
@@ -127,6 +130,7 @@ static float bf16_to_f32(uint16_t h)
 /*       at row bytes 512 + 4g.                                             */
 /*   RoPE (layout 2): input rows of 512 + 64 values; the first 512 as the   */
 /*       scaled layout, the 64 RoPE values copied as bf16 to bytes 528..655. */
+/*   BF16 (layout 3): the 512 bf16 values copied unchanged (no cast).       */
 /* ------------------------------------------------------------------------ */
 int64_t orc_kv_write(const uint16_t *kv, int64_t n, int64_t kv_row_stride,
                      const int64_t *slot_mapping, uint8_t *pool,
@@ -134,7 +138,8 @@ int64_t orc_kv_write(const uint16_t *kv, int64_t n, int64_t kv_row_stride,
 {
     int64_t errors = 0;
     int64_t row_bytes = layout == 0 ? ORC_RAW_BYTES
-                        : layout == 1 ? ORC_SCALED_BYTES : ORC_ROPE_BYTES;
+                        : layout == 1 ? ORC_SCALED_BYTES
+                        : layout == 2 ? ORC_ROPE_BYTES : ORC_BF16_BYTES;
 
     for (int64_t i = 0; i < n; i++) {
         int64_t slot = slot_mapping[i];
@@ -148,7 +153,12 @@ int64_t orc_kv_write(const uint16_t *kv, int64_t n, int64_t kv_row_stride,
             continue;
         }
         dst = pool + slot * row_bytes;
-        if (layout == 0) {
+        if (layout == 3) {
+            for (int d = 0; d < ORC_D; d++) {
+                dst[2 * d] = (uint8_t)(src[d] & 0xff);
+                dst[2 * d + 1] = (uint8_t)(src[d] >> 8);
+            }
+        } else if (layout == 0) {
             for (int d = 0; d < ORC_D; d++)
                 dst[d] = orc_fp8_encode(bf16_to_f32(src[d]));
         } else {
@@ -319,7 +329,10 @@ static void rope_row(const uint8_t *row, double *xr)
 
 static void dequant_row(const uint8_t *row, int layout, double *x)
 {
-    if (layout == 0) {
+    if (layout == 3) {
+        for (int d = 0; d < ORC_D; d++)
+            x[d] = bf16_to_f32((uint16_t)(row[2 * d] | (row[2 * d + 1] << 8)));
+    } else if (layout == 0) {
         for (int d = 0; d < ORC_D; d++)
             x[d] = orc_fp8_decode(row[d]);
     } else {
@@ -367,7 +380,8 @@ struct attn_job {
 static void attn_tokens(struct attn_job *jb)
 {
     int64_t row_bytes = jb->layout == 0 ? ORC_RAW_BYTES
-                        : jb->layout == 1 ? ORC_SCALED_BYTES : ORC_ROPE_BYTES;
+                        : jb->layout == 1 ? ORC_SCALED_BYTES
+                        : jb->layout == 2 ? ORC_ROPE_BYTES : ORC_BF16_BYTES;
     int rope = jb->layout == 2 ? ORC_ROPE : 0;   /* query row: ORC_D + rope */
     double *x = malloc(sizeof(double) * (size_t)jb->K * ORC_D);
     double *xr = malloc(sizeof(double) * (size_t)jb->K * ORC_ROPE);

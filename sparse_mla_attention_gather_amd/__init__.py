@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsa_mi355x.so")
 
 # enums of include/dsa.h
-DSA_KV_RAW_FP8_512, DSA_KV_SCALED_FP8_528, DSA_KV_SCALED_FP8_656 = 0, 1, 2
+DSA_KV_RAW_FP8_512, DSA_KV_SCALED_FP8_528, DSA_KV_SCALED_FP8_656, DSA_KV_BF16_1024 = 0, 1, 2, 3
 DSA_BF16, DSA_FP32, DSA_FP8_E4M3FN, DSA_FP8_E4M3FNUZ = 0, 1, 2, 3
 STATUS = ["DSA_OK", "DSA_ERR_NULL", "DSA_ERR_SHAPE", "DSA_ERR_WIDTH_MISMATCH",
           "DSA_ERR_LAYOUT", "DSA_ERR_DTYPE", "DSA_ERR_ALIGN",

@@ -42,7 +42,7 @@ int32_t check_fp8_format(int32_t f) {
 
 int32_t check_layout(int32_t layout) {
     return (layout == DSA_KV_RAW_FP8_512 || layout == DSA_KV_SCALED_FP8_528 ||
-            layout == DSA_KV_SCALED_FP8_656)
+            layout == DSA_KV_SCALED_FP8_656 || layout == DSA_KV_BF16_1024)
                ? DSA_OK
                : DSA_ERR_LAYOUT;
 }
@@ -66,8 +66,9 @@ int32_t validate_attn(const void *q, int32_t q_dtype, const float *q_scale,
     if (rope_dim != rope_of(layout)) return DSA_ERR_LAYOUT;
     if ((st = check_fp8_format(fp8_format))) return st;
     if (q_dtype != DSA_BF16 && q_dtype != DSA_FP8_E4M3FN) return DSA_ERR_DTYPE;
-    // the FP8 query path is NoPE-only [Q8, Modifications]
-    if (rope_dim != 0 && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    // the FP8 query path is NoPE-only [Q8, Modifications], and FP8 codes
+    // meet FP8 rows only
+    if ((rope_dim != 0 || layout == DSA_KV_BF16_1024) && q_dtype != DSA_BF16) return DSA_ERR_DTYPE;
     if (out_dtype != DSA_BF16 && out_dtype != DSA_FP32) return DSA_ERR_DTYPE;
     if (T < 0 || H < 1 || H > 128) return DSA_ERR_SHAPE;
     if (K <= 0 || K % 128 != 0 || K > 65536) return DSA_ERR_SHAPE;
@@ -147,6 +148,7 @@ int32_t dsa_kv_row_bytes(int32_t layout) {
     if (layout == DSA_KV_RAW_FP8_512) return 512;
     if (layout == DSA_KV_SCALED_FP8_528) return 528;
     if (layout == DSA_KV_SCALED_FP8_656) return 656;
+    if (layout == DSA_KV_BF16_1024) return 1024;
     return -1;
 }
 

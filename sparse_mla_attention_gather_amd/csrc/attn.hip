@@ -96,13 +96,15 @@ constexpr float kNoMax = -1.0e30f;
 
 // LDS map (bytes) for NT head tiles of 16 and a row layout.  656-byte rows
 // add a ring of RoPE parts (64 rows x 128 B per tile) and, to stay within the
-// 160 KB of a CU, keep three tile buffers instead of four.
+// 160 KB of a CU, keep three tile buffers instead of four; 1024-byte bf16
+// rows keep two buffers of 64 KB.
 template <int NT, int LAYOUT>
 struct Lds {
     static constexpr int kHB = 16 * NT;
-    static constexpr int kNB = LAYOUT == 2 ? 3 : kNBuf;          // tile buffers
+    static constexpr int kNB = LAYOUT == 2 ? 3 : LAYOUT == 3 ? 2 : kNBuf;   // tile buffers
     static constexpr int kParts = 2;                             // QK dim parts
-    static constexpr int kBufBytes = kTile * 512;                // 32 KB payload
+    static constexpr int kRowPitch = LAYOUT == 3 ? 1024 : 512;   // LDS bytes per row
+    static constexpr int kBufBytes = kTile * kRowPitch;          // 32 KB (bf16 rows: 64 KB)
     static constexpr int kScBytes = kTile * 16;                  // 1 KB scales
     static constexpr int kRopeTile = kTile * 2 * kRopeDim;       // 8 KB RoPE parts
     static constexpr int kOffScales = kNB * kBufBytes;
@@ -136,7 +138,7 @@ struct Lds {
 // slot).  64 distinct zero rows, picked by the tile row, keep these reads off
 // a single set of L2 lines.
 constexpr int kZeroRows = 64;
-__device__ __attribute__((aligned(16))) const uint8_t kZeroRow[kZeroRows * kRopeRowBytes] = {};
+__device__ __attribute__((aligned(16))) const uint8_t kZeroRow[kZeroRows * kBf16RowBytes] = {};
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
@@ -229,6 +231,7 @@ struct TileSlots {
     int32_t row[kLoadsRaw];
     int32_t sc;     // the scale words' row (lanes 0-3)
     int32_t rp;     // the RoPE part's row (lanes 0-31)
+    int32_t r4[kRowsPerWave];   // bf16 rows: the wave's rows, one per instruction
 };
 
 template <int LAYOUT>
@@ -237,8 +240,10 @@ __device__ __forceinline__ TileSlots read_slots(const int32_t *slots, int tile_b
     const int r0 = kRowsPerWave * w;
 #pragma unroll
     for (int k = 0; k < kLoadsRaw; k++) s.row[k] = slots[tile_base + r0 + 2 * k + (lane >> 5)];
-    s.sc = LAYOUT >= 1 ? slots[tile_base + r0 + (lane & (kRowsPerWave - 1))] : 0;
+    s.sc = (LAYOUT == 1 || LAYOUT == 2) ? slots[tile_base + r0 + (lane & (kRowsPerWave - 1))] : 0;
     s.rp = LAYOUT == 2 ? slots[tile_base + r0 + ((lane >> 3) & (kRowsPerWave - 1))] : 0;
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; k++) s.r4[k] = LAYOUT == 3 ? slots[tile_base + r0 + k] : 0;
     return s;
 }
 
@@ -253,9 +258,23 @@ template <int LAYOUT, int NT>
 __device__ __forceinline__ void issue_tile(const AttnArgs &a, uint32_t lds0, const TileSlots &s,
                                            int buf, int sbuf, int w, int lane) {
     using L = Lds<NT, LAYOUT>;
-    constexpr int64_t kRow = LAYOUT == 0 ? kRawBytes : LAYOUT == 1 ? kScaledBytes : kRopeRowBytes;
+    constexpr int64_t kRow = LAYOUT == 0 ? kRawBytes : LAYOUT == 1 ? kScaledBytes
+                             : LAYOUT == 2 ? kRopeRowBytes : kBf16RowBytes;
     const int r0 = kRowsPerWave * w;
-    const uint32_t dst = lds0 + buf * L::kBufBytes + r0 * 512;
+    const uint32_t dst = lds0 + buf * L::kBufBytes + r0 * L::kRowPitch;
+    if constexpr (LAYOUT == 3) {
+        // one 1024-byte row per instruction: lane l -> position l, holding
+        // chunk l ^ swz(row)
+#pragma unroll
+        for (int k = 0; k < kRowsPerWave; k++) {
+            const int r = r0 + k;
+            const int chunk = lane ^ swz(r);
+            const uint8_t *src = s.r4[k] >= 0 ? a.pool + (int64_t)s.r4[k] * kRow + chunk * 16
+                                              : kZeroRow + r * kRow + chunk * 16;
+            dma16(src, dst + k * 1024);
+        }
+        return;
+    }
     const int pos = lane & 31;
 #pragma unroll
     for (int k = 0; k < kLoadsRaw; k++) {
@@ -265,7 +284,7 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, uint32_t lds0, con
                                            : kZeroRow + r * kRow + chunk * 16;
         dma16(src, dst + k * 1024);
     }
-    if (LAYOUT >= 1) {
+    if (LAYOUT == 1 || LAYOUT == 2) {
         if (lane < kRowsPerWave) {
             const int r = r0 + lane;
             const uint8_t *src = s.sc >= 0 ? a.pool + (int64_t)s.sc * kRow + kD
@@ -295,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     constexpr int kSteps8 = kDP / 128;           // FP8 K = 128 steps per part
     constexpr int kGpp = kDP / 128;              // scale groups per part
     constexpr int kChunks = kDP / 16;            // 16-byte row chunks per part
-    constexpr int kXc = kDP / 64;                // of which one lane holds (4 lane groups)
+    constexpr int kXc = LAYOUT == 3 ? kDP / 32 : kDP / 64;   // of which one lane holds (4 lane groups)
     // Schedule.  Pipelined: waves 0-7 score (QK and the owners' softmax),
     // waves 8-15 accumulate PV one tile behind, so the owners' softmax of
     // tile k overlaps the PV of tile k-1 and each tile's operand reads
@@ -311,14 +330,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // PV operands read in their own step (one register set; a tile's buffer
     // is refilled right after its step): 32-head blocks and 656-byte rows,
     // whose extra operands would not fit otherwise
-    constexpr bool kLate = kPipe && (NT == 2 || LAYOUT == 2);
+    constexpr bool kLate = kPipe && (NT == 2 || LAYOUT >= 2);
+    constexpr bool kScaled = LAYOUT == 1 || LAYOUT == 2;   // rows carry group scales
     constexpr int kDT = kPipe ? 4 : 2;           // PV: 16-dim tiles per wave
 #ifndef DSA_FILL0
 #define DSA_FILL0 2
 #endif
     constexpr int kFill0 = DSA_FILL0;            // tiles requested before the first lands
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    constexpr int kLoads = kLoadsRaw + (LAYOUT >= 1 ? 1 : 0) + (LAYOUT == 2 ? 1 : 0);
+    constexpr int kLoads = LAYOUT == 3 ? kRowsPerWave
+                                       : kLoadsRaw + (kScaled ? 1 : 0) + (LAYOUT == 2 ? 1 : 0);
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
@@ -341,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     constexpr bool kRowPair = kPipe && NT == 2 && !QFP8;
     // scoring waves read a tile's row chunks in the tile's own step rather
     // than during the softmax before (possible with kLate's buffer rotation)
-    constexpr bool kOwnStep = kRowPair || (kPipe && LAYOUT == 2);
+    constexpr bool kOwnStep = kRowPair || (kPipe && LAYOUT >= 2);
     constexpr int kRT = kRowPair ? 2 : 1;        // entry quarters a scoring wave scores
     constexpr int kQT = kRowPair ? 1 : (kPipe ? NT : 1);   // head tiles it scores
     const int rh = w & 1;
@@ -526,7 +547,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // tile parity; one set when not pipelined or with kLate).
     u32x4 xc[kRT][kXc];
     u32x4 xcr;                  // 656-byte rows: this lane's RoPE chunk
-    u32x2 tv[kPipe && !kLate ? 2 : 1][2][kDT];
+    // (bf16 rows: eight 16-bit values per operand, u32x4)
+    std::conditional_t<LAYOUT == 3, u32x4, u32x2> tv[kPipe && !kLate ? 2 : 1][2][kDT];
     f32x4 part[kRT * kQT];      // [entry quarter][head tile]
 
     // Wait until this wave's DMA of tile j has landed: `issued` is the last
@@ -546,12 +568,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int rt = 0; rt < kRT; rt++) {
             const int r = 16 * (kRowPair ? 2 * rh + rt : wq) + c;
-            const uint8_t *xr = lds + (j % kNB) * L::kBufBytes + r * 512;
+            const uint8_t *xr = lds + (j % kNB) * L::kBufBytes + r * L::kRowPitch;
             const int sw = swz(r);
 #pragma unroll
             for (int m = 0; m < kXc; m++) {
-                const int ch = QFP8 ? dp * kChunks + (m >> 1) * 8 + g * 2 + (m & 1)
-                                    : dp * kChunks + m * 4 + g;
+                // bf16 rows: step m's 8 dims (the query's d of step m) are the
+                // 16-byte chunk d / 8
+                const int ch = LAYOUT == 3 ? dp * 32 + (m >> 1) * 8 + 2 * g + (m & 1)
+                               : QFP8 ? dp * kChunks + (m >> 1) * 8 + g * 2 + (m & 1)
+                                      : dp * kChunks + m * 4 + g;
                 xc[rt][m] = *reinterpret_cast<const u32x4 *>(xr + ((ch ^ sw) * 16));
             }
             if constexpr (LAYOUT == 2) {
@@ -567,16 +592,40 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     auto read_tv = [&](int j, auto par) {
         constexpr int PAR = decltype(par)::value;
         const uint8_t *xb = lds + (j % kNB) * L::kBufBytes;
+        if constexpr (LAYOUT == 3) {
+            // bf16 rows: the operand's 8 entries ks*32 + g*8 + i of dim
+            // dbase + 16dt + c, one 16-bit read each (chunk dim / 8 of each
+            // entry's row, swizzled by that row)
 #pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-            const int row = ks * 32 + g * 8 + (c >> 1);
-            const uint8_t *rp = xb + row * 512 + (c & 1) * 8;
-            const int sw = swz(row);
+            for (int ks = 0; ks < 2; ks++)
 #pragma unroll
-            for (int dt = 0; dt < kDT; dt++)
-                tv[PAR][ks][dt] = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_i32x2 *>(
-                               LDS_PTR(rp + (((dbase / 16 + dt) ^ sw) * 16)))));
+                for (int dt = 0; dt < kDT; dt++) {
+                    const int dim = dbase + 16 * dt + c;
+                    uint32_t hw[8];
+#pragma unroll
+                    for (int i = 0; i < 8; i++) {
+                        const int e = ks * 32 + g * 8 + i;
+                        hw[i] = *reinterpret_cast<const uint16_t *>(
+                            xb + e * 1024 + (((dim >> 3) ^ swz(e)) * 16) + (dim & 7) * 2);
+                    }
+                    tv[PAR][ks][dt] = u32x4{hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16),
+                                            hw[4] | (hw[5] << 16), hw[6] | (hw[7] << 16)};
+                    // at most two operands' reads in flight (all 64 at once
+                    // would not fit the registers)
+                    if (dt & 1) __builtin_amdgcn_sched_barrier(0);
+                }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                const int row = ks * 32 + g * 8 + (c >> 1);
+                const uint8_t *rp = xb + row * 512 + (c & 1) * 8;
+                const int sw = swz(row);
+#pragma unroll
+                for (int dt = 0; dt < kDT; dt++)
+                    tv[PAR][ks][dt] = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_i32x2 *>(
+                                   LDS_PTR(rp + (((dbase / 16 + dt) ^ sw) * 16)))));
+            }
         }
     };
 
@@ -587,7 +636,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     auto qk = [&](int j) {
         const float *scf = reinterpret_cast<const float *>(lds + L::kOffScales + (j % kNScale) * L::kScBytes);
         float scv[4][kGpp];
-        if constexpr (LAYOUT >= 1) {
+        if constexpr (kScaled) {
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -611,7 +660,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                     float s = 0.0f;
 #pragma unroll
                     for (int k2 = 0; k2 < kSteps8; k2++)
-                        s += LAYOUT == 0 ? accg[k2][i] : accg[k2][i] * scv[i][k2];
+                        s += !kScaled ? accg[k2][i] : accg[k2][i] * scv[i][k2];
                     part[nt][i] = s;
                 }
             }
@@ -619,7 +668,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             // raw rows: two independent chains (even / odd kk) for a single
             // (quarter, head tile) product, else one per product; scaled
             // rows (one of each): one chain per 128-wide scale group
-            constexpr int kCh = (LAYOUT == 0 && kQT > 1) ? 1 : 2;
+            constexpr int kCh = (!kScaled && kQT > 1) ? 1 : 2;
             f32x4 accg[kRT][kQT][2];
 #pragma unroll
             for (int rt = 0; rt < kRT; rt++)
@@ -629,11 +678,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             for (int rt = 0; rt < kRT; rt++)
 #pragma unroll
                 for (int kk = 0; kk < kSteps; kk++) {
-                    const int q = LAYOUT == 0 ? (kCh == 2 ? (kk & 1) : 0)
-                                              : (kGpp == 1 ? (kk & 1) : (kk >> 2));
-                    const u32x4 &ch = xc[rt][kk >> 1];
-                    const bf16x8 av = (kk & 1) ? e4m3x8_to_bf16(ch[2], ch[3])
-                                               : e4m3x8_to_bf16(ch[0], ch[1]);
+                    const int q = !kScaled ? (kCh == 2 ? (kk & 1) : 0)
+                                           : (kGpp == 1 ? (kk & 1) : (kk >> 2));
+                    bf16x8 av;
+                    if constexpr (LAYOUT == 3) {
+                        av = __builtin_bit_cast(bf16x8, xc[rt][kk]);   // bf16 rows: as read
+                    } else {
+                        const u32x4 &ch = xc[rt][kk >> 1];
+                        av = (kk & 1) ? e4m3x8_to_bf16(ch[2], ch[3]) : e4m3x8_to_bf16(ch[0], ch[1]);
+                    }
 #pragma unroll
                     for (int nt = 0; nt < kQT; nt++)
                         accg[rt][nt][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -650,9 +703,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
                         const f32x4 *ag = accg[rt][nt];
-                        if constexpr (LAYOUT == 0 || kGpp == 1) {
+                        if constexpr (!kScaled || kGpp == 1) {
                             const float s = kCh == 2 ? ag[0][i] + ag[1][i] : ag[0][i];
-                            part[rt * kQT + nt][i] = LAYOUT == 0 ? s : s * scv[i][0];
+                            part[rt * kQT + nt][i] = !kScaled ? s : s * scv[i][0];
                         } else {
                             part[rt * kQT + nt][i] = ag[0][i] * scv[i][0] + ag[1][i] * scv[i][kGpp - 1];
                         }
@@ -704,7 +757,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         const f32x4 mp = *reinterpret_cast<const f32x4 *>(
             lds + L::kOffMq + (par ^ 1) * L::kMqBytes + hh * 16);
         float sc_own = 0.0f;
-        if constexpr (LAYOUT >= 1)
+        if constexpr (kScaled)
             sc_own = reinterpret_cast<const float *>(lds + L::kOffScales + (j % kNScale) * L::kScBytes)[lane * 4 + wq];
         then();
         const int slv[4] = {sl4.x, sl4.y, sl4.z, sl4.w};
@@ -737,12 +790,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             p[i] = __builtin_amdgcn_exp2f(sv[i] - m_own);   // masked: 2^-inf = 0
             l_part += p[i];
         }
-        const f16x2 p01 = {(_Float16)p[0], (_Float16)p[1]};
-        const f16x2 p23 = {(_Float16)p[2], (_Float16)p[3]};
-        const u32x2 pk = {__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+        u32x2 pk;
+        if constexpr (LAYOUT == 3) {
+            // bf16 rows multiply P as bf16 (the PV MFMA takes one type)
+            pk = u32x2{f32_to_bf16_bits(p[0]) | (f32_to_bf16_bits(p[1]) << 16),
+                       f32_to_bf16_bits(p[2]) | (f32_to_bf16_bits(p[3]) << 16)};
+        } else {
+            const f16x2 p01 = {(_Float16)p[0], (_Float16)p[1]};
+            const f16x2 p23 = {(_Float16)p[2], (_Float16)p[3]};
+            pk = u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+        }
         *reinterpret_cast<u32x2 *>(p_w + p_off(hh, 2 * wq + (g >> 1)) + (g & 1) * 8) = pk;
         if (g == 0) mq_w[hh * 4 + wq] = m_own;
-        if constexpr (LAYOUT >= 1) {
+        if constexpr (kScaled) {
             // largest scale of group wq over the tile's 64 entries
             const float smax = max_over_g(dpp_max16(sc_own));
             if (lane == 0) reinterpret_cast<float *>(lds + L::kOffSmax)[par * 4 + wq] = smax;
@@ -811,7 +871,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             }
         }
         float smax = 1.0f;
-        if constexpr (LAYOUT >= 1) {
+        if constexpr (kScaled) {
             // scale group dbase/128 of each entry, normalised by the tile's
             // largest (published with P) so that the f16 operand stays in
             // range; the factor is put back when the tile's product is added
@@ -836,7 +896,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int nt = 0; nt < NT; nt++)
 #pragma unroll
-                for (int ks = 0; ks < 2; ks++) bp[nt][ks] *= (_Float16)fq[nt][ks];
+                for (int ks = 0; ks < 2; ks++) {
+                    if constexpr (LAYOUT == 3) {
+                        // bf16 P: widen, weight in fp32, round back
+                        u32x4 b = __builtin_bit_cast(u32x4, bp[nt][ks]);
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            const float lo = bf16_bits_to_f32(b[e] & 0xffffu) * fq[nt][ks];
+                            const float hi = bf16_bits_to_f32(b[e] >> 16) * fq[nt][ks];
+                            b[e] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+                        }
+                        bp[nt][ks] = __builtin_bit_cast(f16x8, b);
+                    } else {
+                        bp[nt][ks] *= (_Float16)fq[nt][ks];
+                    }
+                }
         }
         pv_smax = smax;
     };
@@ -844,6 +918,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         constexpr int TPAR = decltype(tpar)::value;
 #pragma unroll
         for (int dt = decltype(dt0)::value; dt < decltype(dt1)::value; dt++) {
+            if constexpr (LAYOUT == 3) {
+                // bf16 rows: the gathered operands as they are, bf16 P
+                const bf16x8 bv0 = __builtin_bit_cast(bf16x8, tv[TPAR][0][dt]);
+                const bf16x8 bv1 = __builtin_bit_cast(bf16x8, tv[TPAR][1][dt]);
+#pragma unroll
+                for (int nt = 0; nt < NT; nt++) {
+                    acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        bv0, __builtin_bit_cast(bf16x8, pv_bp[nt][0]), acc[dt][nt], 0, 0, 0);
+                    acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        bv1, __builtin_bit_cast(bf16x8, pv_bp[nt][1]), acc[dt][nt], 0, 0, 0);
+                }
+            } else {
             const f16x8 av0 = e4m3x8_to_f16(tv[TPAR][0][dt][0], tv[TPAR][0][dt][1]);
             const f16x8 av1 = e4m3x8_to_f16(tv[TPAR][1][dt][0], tv[TPAR][1][dt][1]);
 #pragma unroll
@@ -856,6 +942,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                     prt = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, pv_bp[nt][1], prt, 0, 0, 0);
                     acc[dt][nt] += prt * pv_smax;
                 }
+            }
             }
         }
     };
@@ -1235,6 +1322,8 @@ hipError_t launch_attn(const AttnArgs &a_in, int layout, bool q_fp8, bool out_bf
     DSA_DISPATCH(1, true, true)
     DSA_DISPATCH(2, false, false)
     DSA_DISPATCH(2, false, true)
+    DSA_DISPATCH(3, false, false)
+    DSA_DISPATCH(3, false, true)
 #undef DSA_DISPATCH
     return hipErrorInvalidValue;
 }

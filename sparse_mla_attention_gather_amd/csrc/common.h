@@ -27,6 +27,7 @@ constexpr int kScaledBytes = 528;
 // RoPE values (the pages give only the size; this split is the reading)
 constexpr int kRopeDim = 64;
 constexpr int kRopeRowBytes = 656;
+constexpr int kBf16RowBytes = 1024;   // 512 bf16 values, no cast
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
     return __uint_as_float(h16 << 16);

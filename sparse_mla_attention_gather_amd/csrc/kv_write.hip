@@ -6,7 +6,8 @@
 // group-scaled FP8 NoPE KV reads for CUDA TileLang", Motivation: 512 FP8
 // values followed by four fp32 scales, one per 128 values), and the 656-byte
 // RoPE layout the same page says the readers keep (the scaled row followed by
-// the row's 64 RoPE values, copied as bf16).
+// the row's 64 RoPE values, copied as bf16); bf16 rows are stored as given
+// (the 1024-byte pool the raw page compares against).
 //
 // Mapping: one 64-lane wavefront per row; lane l owns elements [8l, 8l+8)
 // (one 16-byte load of bf16, one 8-byte store of codes), so a 128-element
@@ -38,9 +39,13 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
         x[2 * i] = bf16_bits_to_f32(raw[i] & 0xffffu);
         x[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
     }
-    constexpr int64_t kRow = LAYOUT == 0 ? kRawBytes : LAYOUT == 1 ? kScaledBytes : kRopeRowBytes;
+    constexpr int64_t kRow = LAYOUT == 0 ? kRawBytes : LAYOUT == 1 ? kScaledBytes
+                             : LAYOUT == 2 ? kRopeRowBytes : kBf16RowBytes;
     uint8_t *dst = pool + slot * kRow;
-    if (LAYOUT == 0) {
+    if (LAYOUT == 3) {
+        // bf16 rows: the 16 input bytes as they are
+        *reinterpret_cast<u32x4 *>(dst + lane * 16) = raw;
+    } else if (LAYOUT == 0) {
         u32x2 codes = {pack4_e4m3(x[0], x[1], x[2], x[3]),
                        pack4_e4m3(x[4], x[5], x[6], x[7])};
         *reinterpret_cast<u32x2 *>(dst + lane * 8) = codes;
@@ -79,8 +84,11 @@ hipError_t launch_kv_write(const uint16_t *kv, int64_t n, int64_t row_stride,
     else if (layout == 1)
         kv_write_kernel<1><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
             kv, n, row_stride, slot_mapping, pool, num_slots, err_count);
-    else
+    else if (layout == 2)
         kv_write_kernel<2><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+            kv, n, row_stride, slot_mapping, pool, num_slots, err_count);
+    else
+        kv_write_kernel<3><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
             kv, n, row_stride, slot_mapping, pool, num_slots, err_count);
     return hipGetLastError();
 }

@@ -19,7 +19,7 @@ import torch
 import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-RAW, SCALED, ROPE = 0, 1, 2
+RAW, SCALED, ROPE, BF16 = 0, 1, 2, 3
 
 
 # --------------------------------------------------------------------------
@@ -404,6 +404,8 @@ def build_pool(orc, wl: W.Workload, poison=True):
     lat, sc = W.pool_content(wl.seed, len(slots), wl.layout)
     if wl.layout == RAW:
         orc.kv_write(lat, slots, pool, RAW)
+    elif wl.layout == BF16:        # the latents themselves, little-endian bf16
+        pool[slots] = np.ascontiguousarray(lat).view(np.uint8)
     else:
         tmp = np.zeros((len(slots), 512), np.uint8)
         orc.kv_write(lat[:, :512], np.arange(len(slots)), tmp, RAW)
@@ -415,6 +417,8 @@ def build_pool(orc, wl: W.Workload, poison=True):
 
 
 def dequant_pool(pool, layout):
+    if layout == BF16:
+        return f32_from_bf16(np.ascontiguousarray(pool).view(np.uint16)).astype(np.float64)
     x = torch_dec(pool[:, :512])
     if layout in (SCALED, ROPE):
         sc = pool[:, 512:528].copy().view(np.float32).astype(np.float64)
@@ -523,6 +527,35 @@ def pin_writer_rope(orc):
     assert np.array_equal(rope[slots[ok], 528:], np.ascontiguousarray(kv[ok, 512:]).view(np.uint8))
     untouched = np.setdiff1d(np.arange(64), slots[ok])
     assert np.all(rope[untouched] == 0xAB)
+
+
+def pin_writer_bf16(orc):
+    """1024-byte rows: the writer stores the 512 bf16 values unchanged
+    (numpy's byte view of the input), and touches no other slot."""
+    rng = np.random.default_rng(72)
+    n = 30
+    kv = W.normal_bf16(rng, (n, 600))
+    slots = rng.permutation(50)[:n].astype(np.int64)
+    slots[4] = -1
+    pool = np.full((50, 1024), 0xCD, np.uint8)
+    assert orc.kv_write(kv, slots, pool, BF16) == 0
+    ok = slots >= 0
+    assert np.array_equal(pool[slots[ok]], np.ascontiguousarray(kv[ok, :512]).view(np.uint8))
+    assert np.all(pool[np.setdiff1d(np.arange(50), slots[ok])] == 0xCD)
+
+
+def pin_attention_bf16_dense_brute_force(orc):
+    """1024-byte bf16 rows against dense attention over every slot."""
+    for dup in (0.0, 0.3):
+        wl = W.small(64, T=4, H=8, K=128, layout=BF16, seq_len=96, page_size=16,
+                     dup_frac=dup, all_masked=(3,))
+        pool = build_pool(orc, wl)
+        out, lse, err = _run(orc, wl, pool)
+        assert err == 0
+        ref, ref_lse = dense_attention(_qhat(wl), dequant_pool(pool, BF16),
+                                       count_matrix(wl), wl.softmax_scale)
+        _close(out, ref)
+        _close(lse, ref_lse)
 
 
 def pin_attention_rope_dense_brute_force(orc):

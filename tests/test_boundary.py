@@ -49,6 +49,7 @@ def test_row_bytes_match_the_pages():
     assert dsa.dsa_kv_row_bytes(dsa.DSA_KV_RAW_FP8_512) == rows["raw_fp8_nope"]
     assert dsa.dsa_kv_row_bytes(dsa.DSA_KV_SCALED_FP8_528) == rows["scaled_fp8_nope"]
     assert dsa.dsa_kv_row_bytes(dsa.DSA_KV_SCALED_FP8_656) == rows["scaled_fp8_rope"]
+    assert dsa.dsa_kv_row_bytes(dsa.DSA_KV_BF16_1024) == rows["bf16_nope"]
     assert dsa.dsa_kv_row_bytes(7) == -1
     assert rows["topk_multiple"] == 128
 
@@ -108,6 +109,9 @@ REJECT = [
     (dict(layout=dsa.DSA_KV_SCALED_FP8_656, rope_dim=32), "DSA_ERR_LAYOUT"),
     (dict(layout=dsa.DSA_KV_SCALED_FP8_656, rope_dim=64, q_dtype=dsa.DSA_FP8_E4M3FN,
           q_scale=FAKE), "DSA_ERR_DTYPE"),                               # NoPE-only FP8 query
+    (dict(layout=dsa.DSA_KV_BF16_1024, q_dtype=dsa.DSA_FP8_E4M3FN, q_scale=FAKE),
+     "DSA_ERR_DTYPE"),                                                   # FP8 query, bf16 rows
+    (dict(layout=dsa.DSA_KV_BF16_1024, rope_dim=64), "DSA_ERR_LAYOUT"),
     (dict(layout=9), "DSA_ERR_LAYOUT"),
     (dict(fp8_format=dsa.DSA_FP8_E4M3FNUZ), "DSA_ERR_DTYPE"),
     (dict(fp8_format=dsa.DSA_BF16), "DSA_ERR_DTYPE"),
@@ -304,4 +308,12 @@ def test_rope_layout_passes_validation():
         assert st in (dsa.DSA_ERR_DEVICE, dsa.DSA_OK), dsa.dsa_status_string(st)
     st = dsa.dsa_kv_write(**kv_args(layout=dsa.DSA_KV_SCALED_FP8_656, rope_dim=64,
                                     kv_row_stride=576))
+    assert st in (dsa.DSA_ERR_DEVICE, dsa.DSA_OK), dsa.dsa_status_string(st)
+
+
+def test_bf16_layout_passes_validation():
+    for phase in (0, 1):
+        st = call(phase, layout=dsa.DSA_KV_BF16_1024)
+        assert st in (dsa.DSA_ERR_DEVICE, dsa.DSA_OK), dsa.dsa_status_string(st)
+    st = dsa.dsa_kv_write(**kv_args(layout=dsa.DSA_KV_BF16_1024))
     assert st in (dsa.DSA_ERR_DEVICE, dsa.DSA_OK), dsa.dsa_status_string(st)

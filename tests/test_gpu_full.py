@@ -29,7 +29,9 @@ def _materialise(orc, wl, seqs):
     host = np.zeros((wl.num_slots, R), np.uint8)
     slots = wl.page_slots(wl.used_pages(seqs))
     lat, sc = W.pool_content(wl.seed, len(slots), wl.layout)
-    if wl.layout == W.RAW:
+    if wl.layout == W.BF16:
+        host[slots] = np.ascontiguousarray(lat).view(np.uint8)
+    elif wl.layout == W.RAW:
         tmp = np.zeros((len(slots), 512), np.uint8)
         orc.kv_write(lat, np.arange(len(slots)), tmp, W.RAW)
         host[slots] = tmp
@@ -51,7 +53,10 @@ def _materialise(orc, wl, seqs):
                           dtype=torch.int32)
         rows = torch.empty((u.numel(), R), dtype=torch.uint8, device=G.DEV)
         rows[:, :512] = (r + (r >= 0x7F).int()).to(torch.uint8)
-        if R >= 528:
+        if R == 1024:     # bf16 rows: N(0,1) values, not codes
+            rows = torch.randn((u.numel(), 512), generator=gen, device=G.DEV).to(
+                torch.bfloat16).contiguous().view(torch.uint8)
+        if R in (528, 656):
             s = torch.exp2(torch.rand((u.numel(), 4), generator=gen, device=G.DEV) * 8 - 6)
             rows[:, 512:528] = s.contiguous().view(torch.uint8)
         if R == 656:
@@ -115,6 +120,12 @@ def _decode_case(orc, wl, sample):
 def test_decode_batch_full(orc):
     wl = W.decode_batch()
     _decode_case(orc, wl, [0, 9, 31, 40, 63])
+
+
+def test_bf16_decode_full(orc):
+    """The decode batch's shape over 1024-byte bf16 rows."""
+    wl = W.bf16_decode()
+    _decode_case(orc, wl, [0, 21, 50, 63])
 
 
 def test_rope_decode_full(orc):

@@ -184,7 +184,8 @@ def test_attention_small(orc, cfg, phase, qfp8, od):
 
 
 @pytest.mark.parametrize("H", [16, 32])
-@pytest.mark.parametrize("layout", [W.RAW, W.SCALED, W.ROPE], ids=["raw", "scaled", "rope"])
+@pytest.mark.parametrize("layout", [W.RAW, W.SCALED, W.ROPE, W.BF16],
+                         ids=["raw", "scaled", "rope", "bf16"])
 @pytest.mark.parametrize("phase", [0, 1], ids=["decode", "prefill"])
 def test_trailing_masked_entries(orc, layout, phase, H):
     """Rows whose valid entries end early (every later entry -1, as ragged
@@ -209,6 +210,45 @@ def test_trailing_masked_entries(orc, layout, phase, H):
     for t in range(T):
         if widths[t % len(widths)] == 0:
             assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
+
+
+BF16_SMALL = [
+    dict(seed=231, T=5, H=16, K=256, layout=W.BF16),
+    dict(seed=232, T=3, H=8, K=384, layout=W.BF16, dup_frac=0.2, neg_frac=0.3),
+    dict(seed=233, T=40, H=32, K=1664, layout=W.BF16, seq_len=2000, page_size=64),
+    dict(seed=234, T=4, H=16, K=1024, layout=W.BF16, seq_len=1500, page_size=64,
+         physical=True, all_masked=(1,)),
+]
+
+
+@pytest.mark.parametrize("cfg", BF16_SMALL, ids=[f"s{c['seed']}" for c in BF16_SMALL])
+@pytest.mark.parametrize("phase", [0, 1], ids=["decode", "prefill"])
+@pytest.mark.parametrize("od", [dsa.DSA_FP32, dsa.DSA_BF16], ids=["f32", "bf16"])
+def test_attention_bf16_rows_small(orc, cfg, phase, od):
+    """1024-byte bf16 rows (no FP8 anywhere) against the oracle."""
+    wl = W.small(**cfg)
+    pool = P.build_pool(orc, wl)
+    ref, ref_lse, ref_err = _oracle_attn(orc, wl, pool)
+    out, lse, err = G.run_attn(G.DevInputs(wl), G.dev(pool), phase=phase, out_dtype=od)
+    assert err == ref_err
+    G.assert_attn_close(out, ref, od, where=str(cfg))
+    G.assert_lse_close(lse, ref_lse, where=str(cfg))
+    for t in cfg.get("all_masked", ()):
+        assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
+
+
+def test_writer_bf16_rows(orc):
+    """The writer on 1024-byte rows stores the bf16 values unchanged."""
+    rng = np.random.default_rng(18)
+    n, stride = 200, 528
+    kv = W.normal_bf16(rng, (n, stride))
+    slots = rng.permutation(256)[:n].astype(np.int64)
+    slots[::13] = -1
+    ref = np.full((256, 1024), 0x3C, np.uint8)
+    assert orc.kv_write(kv, slots, ref, W.BF16) == 0
+    pool = torch.full((256, 1024), 0x3C, dtype=torch.uint8, device=G.DEV)
+    assert G.run_kv_write(kv, slots, pool, W.BF16) == 0
+    assert np.array_equal(G.host(pool), ref)
 
 
 ROPE_SMALL = [

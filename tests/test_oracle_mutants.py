@@ -75,6 +75,9 @@ MUTANTS = [
     ("rope_term_dropped", "dot += qh[ORC_D + r] * xr[(int64_t)j * ORC_ROPE + r];",
      "dot += 0.0 * qh[ORC_D + r] * xr[(int64_t)j * ORC_ROPE + r];"),
     ("rope_byte_order", "(row[ORC_SCALED_BYTES + 2 * r + 1] << 8)", "(row[ORC_SCALED_BYTES + 2 * r + 1] << 7)"),
+    ("bf16_row_byte_order", "x[d] = bf16_to_f32((uint16_t)(row[2 * d] | (row[2 * d + 1] << 8)));",
+     "x[d] = bf16_to_f32((uint16_t)(row[2 * d + 1] | (row[2 * d] << 8)));"),
+    ("bf16_writer_high_byte", "dst[2 * d + 1] = (uint8_t)(src[d] >> 8);", "dst[2 * d + 1] = (uint8_t)(src[d] >> 9);"),
     ("writer_rope_not_copied", "dst[ORC_SCALED_BYTES + 2 * r] = (uint8_t)(src[ORC_D + r] & 0xff);",
      "dst[ORC_SCALED_BYTES + 2 * r] = 0;"),
     ("query_fp8_scale_ignored", "(double)jb->q_scale;", "1.0;"),

@@ -20,8 +20,8 @@ from typing import Optional
 import numpy as np
 
 D = 512
-RAW, SCALED, ROPE = 0, 1, 2
-ROW_BYTES = {RAW: 512, SCALED: 528, ROPE: 656}
+RAW, SCALED, ROPE, BF16 = 0, 1, 2, 3
+ROW_BYTES = {RAW: 512, SCALED: 528, ROPE: 656, BF16: 1024}
 ROPE_DIM = 64            # bf16 RoPE values after the 528-byte part of a 656-byte row
 POISON = 0xFF  # FP8 S.1111.111 is NaN, and 0xFFFFFFFF is an fp32 NaN
 
@@ -181,6 +181,15 @@ def rope_decode(seed: int = 6) -> Workload:
                     normal_bf16(r_x, (wl.T, D + ROPE_DIM)), wl.slot_mapping, seed=seed)
 
 
+def bf16_decode(seed: int = 7) -> Workload:
+    """The decode batch's shape over 1024-byte bf16 rows (the uncompressed pool
+    the FP8 rows halve)."""
+    wl = decode_batch(seed)
+    return Workload("bf16_decode", wl.T, wl.H, wl.K, BF16, wl.page_size, wl.num_slots,
+                    wl.page_table, wl.seq_lens, None, wl.topk, wl.q, softmax_scale_512(),
+                    wl.kv_new, wl.slot_mapping, seed=seed)
+
+
 def scaled_decode(seed: int = 3) -> Workload:
     """128 sequences x 32768 tokens, 528-byte group-scaled rows in a 2^23-slot
     pool (half the pages used).  H=16, bf16 q.  Each top-k row: 1843 distinct
@@ -280,6 +289,7 @@ NAMED = {
     "q8_prefill": q8_prefill,
     "mixed_decode": mixed_decode,
     "rope_decode": rope_decode,
+    "bf16_decode": bf16_decode,
 }
 
 
