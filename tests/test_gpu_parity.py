@@ -296,6 +296,37 @@ def test_writer_rope_rows(orc):
     assert len(bad[0]) == 0, (len(bad[0]), bad[0][:4], bad[1][:4])
 
 
+@pytest.mark.parametrize("phase", [0, 1], ids=["decode", "prefill"])
+@pytest.mark.parametrize("layout", [W.RAW, W.SCALED], ids=["raw", "scaled"])
+def test_attention_most_heads(orc, layout, phase):
+    """H = 128, the most heads the C ABI accepts (raw: four 32-head
+    blocks; 528-byte rows: eight 16-head blocks)."""
+    wl = W.small(241 + layout, T=2, H=128, K=256, layout=layout, seq_len=400)
+    pool = P.build_pool(orc, wl)
+    ref, ref_lse, ref_err = _oracle_attn(orc, wl, pool)
+    out, lse, err = G.run_attn(G.DevInputs(wl), G.dev(pool), phase=phase)
+    assert err == ref_err
+    G.assert_attn_close(out, ref, where=f"H=128 layout {layout}")
+    G.assert_lse_close(lse, ref_lse)
+
+
+@pytest.mark.parametrize("phase", [0, 1], ids=["decode", "prefill"])
+def test_attention_widest_topk(orc, phase):
+    """K = 65536, the widest top-k list: 32 splits of 2048 entries merged in
+    chunks of 8; page size 16 gives a page-table row (4375 pages) too long to
+    stage in LDS, so the indices resolve through direct page-table loads."""
+    wl = W.small(251, T=2, H=16, K=65536, layout=W.RAW, seq_len=70000, page_size=16,
+                 neg_frac=0.02)
+    print(f"case widest top-k: T={wl.T} H={wl.H} K={wl.K} pages={wl.page_table.shape[1]}",
+          flush=True)
+    pool = P.build_pool(orc, wl)
+    ref, ref_lse, ref_err = _oracle_attn(orc, wl, pool)
+    out, lse, err = G.run_attn(G.DevInputs(wl), G.dev(pool), phase=phase)
+    assert err == ref_err
+    G.assert_attn_close(out, ref, where="K=65536")
+    G.assert_lse_close(lse, ref_lse)
+
+
 def test_invalid_indices_are_masked_and_counted(orc):
     wl = W.small(301, T=4, H=16, K=256, neg_frac=0.25, seq_len=120)
     bad = wl.topk.copy()

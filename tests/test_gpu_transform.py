@@ -52,6 +52,7 @@ CASES = [
     (5, 9, 3000, 4096, 32, 120, 0.3, True, True),
     (6, 1, 256, 384, 64, 8, 1.0, True, False),       # every entry padding
     (7, 33, 777, 896, 128, 10, 0.0, True, False),    # ragged tail of a pass
+    (8, 2, 65536, 65536, 64, 1100, 0.1, True, False),  # the widest row
 ]
 
 
