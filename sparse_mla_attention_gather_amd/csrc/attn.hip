@@ -119,13 +119,17 @@ struct Lds {
     static constexpr int kOffMq = kOffP + 2 * kPBytes;
     static constexpr int kMqBytes = kHB * 16;
     static constexpr int kOffRedL = kOffMq + 2 * kMqBytes;       // [kHB][4] fp32
-    // 528-byte rows: largest scale of each 128-wide group over a tile, two
-    // tiles (by parity)
+    // group-scaled rows: running largest scale of each 128-wide group (the
+    // PV operand's reference), two tiles (by parity)
     static constexpr int kOffSmax = kOffRedL + kHB * 16;
     // per head and quarter: 1 when the quarter's maximum did not move this
     // tile (then it equals the reference maximum), two tiles (by parity)
     static constexpr int kOffFlags = kOffSmax + 2 * 16;
-    static constexpr int kOffRope = kOffFlags + 2 * kHB * 4;     // 16-byte aligned
+    // group-scaled rows: f16 factor scale / reference of each entry and
+    // group ([4][64]), two tiles (by parity)
+    static constexpr int kOffFac = kOffFlags + 2 * kHB * 4;
+    static constexpr int kFacBytes = 4 * kTile * 2;
+    static constexpr int kOffRope = kOffFac + (LAYOUT == 1 || LAYOUT == 2 ? 2 * kFacBytes : 0);
     static constexpr int kBytes = kOffRope + (LAYOUT == 2 ? kNB * kRopeTile : 0);
     // the token's page-table row is staged over the sp and P areas
     static constexpr int kPtPer = (kSpBytes + 2 * kPBytes) / 4 / kThreads;
@@ -533,8 +537,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // over their quarter's entries and the lane's share l_part of the
     // denominator (relative to m_own).  Every wave: the reference maximum
     // m_ref[nt] of head nt*16+c that O is accumulated against.
+    // Group-scaled rows: the owners of head tile 0 keep the running largest
+    // scale of group wq (s_run); the PV operand of an entry is P times
+    // scale / s_run, and O is accumulated in units of the reference s_ref
+    // (the wave's group's s_run, rescaled when it grows).
     float m_own = kNoMax, l_part = 0.0f;
     float m_ref[NT];
+    float s_run = 0.0f, s_ref = 0.0f;
     f32x4 acc[kDT][NT];
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) {
@@ -803,9 +812,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         *reinterpret_cast<u32x2 *>(p_w + p_off(hh, 2 * wq + (g >> 1)) + (g & 1) * 8) = pk;
         if (g == 0) mq_w[hh * 4 + wq] = m_own;
         if constexpr (kScaled) {
-            // largest scale of group wq over the tile's 64 entries
-            const float smax = max_over_g(dpp_max16(sc_own));
-            if (lane == 0) reinterpret_cast<float *>(lds + L::kOffSmax)[par * 4 + wq] = smax;
+            // running largest scale of group wq (this tile's 64 entries one
+            // per lane), then each entry's factor scale / s_run (at most 1,
+            // so that P times it stays within f16); one owner per group
+            s_run = fmaxf(s_run, max_over_g(dpp_max16(sc_own)));
+            if (ht == 0) {
+                const float inv = s_run > 0.0f ? __builtin_amdgcn_rcpf(s_run) : 0.0f;
+                reinterpret_cast<_Float16 *>(lds + L::kOffFac + par * L::kFacBytes)[wq * kTile + lane] =
+                    (_Float16)fminf(sc_own * inv, 1.0f);
+                if (lane == 0) reinterpret_cast<float *>(lds + L::kOffSmax)[par * 4 + wq] = s_run;
+            }
         }
     };
     auto nothing = [] {};
@@ -820,12 +836,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // tv[TPAR].  The pipelined schedule splits the dim tiles over its two
     // phases.
     f16x8 pv_bp[NT][2];
-    float pv_smax = 1.0f;
     auto pv_prep = [&](int j) {
         const int ppar = j & 1;
         const float *mq_lds = reinterpret_cast<const float *>(lds + L::kOffMq + ppar * L::kMqBytes);
         const uint8_t *p_lds = lds + L::kOffP + ppar * L::kPBytes;
-        const float *scf = reinterpret_cast<const float *>(lds + L::kOffScales + (j % kNScale) * L::kScBytes);
         // While every quarter kept the previous reference (all four flags
         // set) the reference, O and P stay as they are.  Otherwise: m_ref
         // takes the largest quarter maximum (O rescaled when it moves) and
@@ -870,28 +884,28 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                     for (int dt = 0; dt < kDT; dt++) acc[dt][nt] *= alpha[nt];
             }
         }
-        float smax = 1.0f;
         if constexpr (kScaled) {
-            // scale group dbase/128 of each entry, normalised by the tile's
-            // largest (published with P) so that the f16 operand stays in
-            // range; the factor is put back when the tile's product is added
-            // to O
+            // the group's running largest scale (uniform): O moves to the
+            // new reference when it grows; then P times each entry's factor
+            // scale / s_run, published by the group's owner
             const int grp = dbase >> 7;
-            smax = reinterpret_cast<const float *>(lds + L::kOffSmax)[ppar * 4 + grp];
-            const float inv = smax > 0.0f ? 1.0f / smax : 0.0f;
+            const float sr = reinterpret_cast<const float *>(lds + L::kOffSmax)[ppar * 4 + grp];
+            const f16x8 *fac = reinterpret_cast<const f16x8 *>(lds + L::kOffFac + ppar * L::kFacBytes +
+                                                                (grp * kTile + g * 8) * 2);
+            const f16x8 fk[2] = {fac[0], fac[32 / 8]};
+            if (sr > s_ref) {
+                const float beta = s_ref * __builtin_amdgcn_rcpf(sr);
 #pragma unroll
-            for (int ks = 0; ks < 2; ks++) {
-                float sc[8];
+                for (int nt = 0; nt < NT; nt++)
 #pragma unroll
-                for (int r = 0; r < 8; r++) sc[r] = scf[(ks * 32 + g * 8 + r) * 4 + grp] * inv;
-#pragma unroll
-                for (int nt = 0; nt < NT; nt++) {
-                    f16x8 fac;
-#pragma unroll
-                    for (int r = 0; r < 8; r++) fac[r] = (_Float16)(sc[r] * fq[nt][ks]);
-                    bp[nt][ks] *= fac;
-                }
+                    for (int dt = 0; dt < kDT; dt++) acc[dt][nt] *= beta;
+                s_ref = sr;
             }
+#pragma unroll
+            for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++)
+                    bp[nt][ks] *= reweight ? fk[ks] * (_Float16)fq[nt][ks] : fk[ks];
         } else if (reweight) {
 #pragma unroll
             for (int nt = 0; nt < NT; nt++)
@@ -912,7 +926,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                     }
                 }
         }
-        pv_smax = smax;
     };
     auto pv_mma = [&](auto tpar, auto dt0, auto dt1) {
         constexpr int TPAR = decltype(tpar)::value;
@@ -934,14 +947,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             const f16x8 av1 = e4m3x8_to_f16(tv[TPAR][1][dt][0], tv[TPAR][1][dt][1]);
 #pragma unroll
             for (int nt = 0; nt < NT; nt++) {
-                if constexpr (LAYOUT == 0) {
-                    acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, pv_bp[nt][0], acc[dt][nt], 0, 0, 0);
-                    acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, pv_bp[nt][1], acc[dt][nt], 0, 0, 0);
-                } else {
-                    f32x4 prt = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, pv_bp[nt][0], f32x4{0, 0, 0, 0}, 0, 0, 0);
-                    prt = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, pv_bp[nt][1], prt, 0, 0, 0);
-                    acc[dt][nt] += prt * pv_smax;
-                }
+                acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, pv_bp[nt][0], acc[dt][nt], 0, 0, 0);
+                acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, pv_bp[nt][1], acc[dt][nt], 0, 0, 0);
             }
             }
         }
@@ -985,7 +992,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 // the split's normalised output o / l (raw rows: f16, whose
                 // range holds any average of E4M3 values; 528-byte rows:
                 // fp32), then (m, l)
-                const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+                const float inv = (l_tot > 0.0f ? 1.0f / l_tot : 0.0f) * (kScaled ? s_ref : 1.0f);
                 const int64_t po = (th * a.n_splits + split) * kD + dbase + 4 * g;
 #pragma unroll
                 for (int dt = 0; dt < kDT; dt++) {
@@ -1006,7 +1013,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                     ml[1] = l_tot;
                 }
             } else {
-                const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+                const float inv = (l_tot > 0.0f ? 1.0f / l_tot : 0.0f) * (kScaled ? s_ref : 1.0f);
                 const int64_t base = th * kD + dbase + 4 * g;
 #pragma unroll
                 for (int dt = 0; dt < kDT; dt++) {
