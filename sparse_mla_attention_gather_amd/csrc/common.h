@@ -56,10 +56,69 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
     return sign | (e << 3) | m;
 }
 
-// Four fp32 -> four E4M3FN codes packed little-endian in a uint32.
-__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+// Four fp32 -> four E4M3FN codes packed little-endian in a uint32 (f32_to_e4m3
+// on each).
+__device__ __forceinline__ uint32_t pack4_e4m3_sw(float a, float b, float c, float d) {
     return f32_to_e4m3(a) | (f32_to_e4m3(b) << 8) | (f32_to_e4m3(c) << 16) |
            (f32_to_e4m3(d) << 24);
+}
+
+// The same codes by the gfx950 converter, for inputs that are not NaN.
+// v_cvt_pk_fp8_f32 rounds to nearest even exactly as f32_to_e4m3 does but
+// turns magnitudes above 464 into NaN; clamping to +-448 first (v_med3) makes
+// it saturate like f32_to_e4m3 for every finite value and +-inf (compared on
+// the device over all 2^32 fp32 patterns).  The clamp does not return NaN.
+__device__ __forceinline__ uint32_t pack4_e4m3_hw(float a, float b, float c, float d) {
+    const auto clamp = [](float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(a), clamp(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(c), clamp(d), w, true);
+    return (uint32_t)w;
+}
+
+// Eight fp32 -> eight E4M3FN codes: the converter, or f32_to_e4m3 on the
+// (normally never taken) branch for a group holding a NaN.
+__device__ __forceinline__ u32x2 encode8(const float (&x)[8]) {
+    bool nan = false;
+#pragma unroll
+    for (int i = 0; i < 8; i++) nan |= __builtin_isnan(x[i]);
+    // wave-uniform branch (a ballot): kept as a branch, not blended per lane
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(nan) != 0, 0))
+        return u32x2{pack4_e4m3_sw(x[0], x[1], x[2], x[3]), pack4_e4m3_sw(x[4], x[5], x[6], x[7])};
+    return u32x2{pack4_e4m3_hw(x[0], x[1], x[2], x[3]), pack4_e4m3_hw(x[4], x[5], x[6], x[7])};
+}
+
+// Codes of the IEEE quotients fp32(x[i] / s) for a divisor used many times,
+// with r = 1/s (IEEE, computed once; r_ok: s and r normal).  q = x * r is
+// within two fp32 ulps of the IEEE quotient (relative error <= 2^-23 for
+// normal s and q), so both have the same code unless q lies within a few
+// ulps of a point halfway between two codes (fp32 mantissa bits 19..0 near
+// 0x80000 in the normal band) or in the subnormal band (0 < |q| < 2^-6).  A
+// wave holding such a value, a NaN, or a divisor without a usable 1/s takes
+// the IEEE division and f32_to_e4m3 for all its values instead (a
+// wave-uniform branch; a few percent of the waves for normally distributed
+// data).
+__device__ __forceinline__ u32x2 encode8_div(const float (&x)[8], float s, float r, bool r_ok) {
+    float q[8];
+    bool slow = !r_ok;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        q[i] = x[i] * r;
+        const float m = fabsf(q[i]);
+        const uint32_t lo = (__float_as_uint(q[i]) - 0x7fff8u) & 0xfffffu;
+        slow |= (m < 0x1p-6f && m != 0.0f) | (lo < 16u) | (m != m);
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(slow) != 0, 0)) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) q[i] = x[i] / s;
+        return u32x2{pack4_e4m3_sw(q[0], q[1], q[2], q[3]), pack4_e4m3_sw(q[4], q[5], q[6], q[7])};
+    }
+    return u32x2{pack4_e4m3_hw(q[0], q[1], q[2], q[3]), pack4_e4m3_hw(q[4], q[5], q[6], q[7])};
+}
+
+// 1/s is usable by encode8_div: s and 1/s normal and finite.
+__device__ __forceinline__ bool recip_ok(float s) {
+    const float m = fabsf(s);
+    return m >= 0x1p-120f && m <= 0x1p120f;
 }
 
 // Exact E4M3FN -> bf16 / f16 conversions of the two codes in the low (hi =

@@ -46,9 +46,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
         // bf16 rows: the 16 input bytes as they are
         *reinterpret_cast<u32x4 *>(dst + lane * 16) = raw;
     } else if (LAYOUT == 0) {
-        u32x2 codes = {pack4_e4m3(x[0], x[1], x[2], x[3]),
-                       pack4_e4m3(x[4], x[5], x[6], x[7])};
-        *reinterpret_cast<u32x2 *>(dst + lane * 8) = codes;
+        *reinterpret_cast<u32x2 *>(dst + lane * 8) = encode8(x);
     } else {
         float amax = 0.0f;
 #pragma unroll
@@ -57,12 +55,9 @@ __global__ __launch_bounds__(256) void kv_write_kernel(
 #pragma unroll
         for (int s = 1; s < 16; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s));
         const float scale = amax == 0.0f ? 1.0f : amax / 448.0f;   // IEEE division
-        float y[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) y[i] = x[i] / scale;
-        u32x2 codes = {pack4_e4m3(y[0], y[1], y[2], y[3]),
-                       pack4_e4m3(y[4], y[5], y[6], y[7])};
-        *reinterpret_cast<u32x2 *>(dst + lane * 8) = codes;
+        // codes of fp32(x / scale), the IEEE quotient
+        *reinterpret_cast<u32x2 *>(dst + lane * 8) =
+            encode8_div(x, scale, 1.0f / scale, recip_ok(scale));
         if ((lane & 15) == 0)
             *reinterpret_cast<float *>(dst + kD + 4 * (lane >> 4)) = scale;
         if (LAYOUT == 2 && lane < kRopeDim / 8) {

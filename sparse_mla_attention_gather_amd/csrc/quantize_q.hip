@@ -36,21 +36,48 @@ __device__ __forceinline__ float block_max(float v, float *red) {
     return v;
 }
 
+// Each thread keeps kQUnroll 16-byte loads in flight per pass (grid-stride
+// over 8-element vectors), so the stream is bandwidth- rather than
+// latency-bound.
+constexpr int kQUnroll = 4;
+
+__device__ __forceinline__ float amax8(u32x4 raw) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        m = fmaxf(m, fabsf(bf16_bits_to_f32(raw[i] & 0xffffu)));
+        m = fmaxf(m, fabsf(bf16_bits_to_f32(raw[i] >> 16)));
+    }
+    return m;
+}
+
 __global__ __launch_bounds__(kQThreads) void q_amax_kernel(
     const uint16_t *__restrict__ q, int64_t n_vec, float *__restrict__ partials) {
     __shared__ float red[kQThreads / 64];
+    const u32x4 *qv = reinterpret_cast<const u32x4 *>(q);
+    const int64_t stride = (int64_t)gridDim.x * kQThreads;
     float m = 0.0f;
     for (int64_t v = (int64_t)blockIdx.x * kQThreads + threadIdx.x; v < n_vec;
-         v += (int64_t)gridDim.x * kQThreads) {
-        const u32x4 raw = reinterpret_cast<const u32x4 *>(q)[v];
+         v += kQUnroll * stride) {
+        u32x4 raw[kQUnroll];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            m = fmaxf(m, fabsf(bf16_bits_to_f32(raw[i] & 0xffffu)));
-            m = fmaxf(m, fabsf(bf16_bits_to_f32(raw[i] >> 16)));
-        }
+        for (int u = 0; u < kQUnroll; u++)
+            raw[u] = v + u * stride < n_vec ? qv[v + u * stride] : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < kQUnroll; u++) m = fmaxf(m, amax8(raw[u]));
     }
     m = block_max(m, red);
     if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+__device__ __forceinline__ u32x2 encode_vec(u32x4 raw, float scale, float rs, bool rs_ok) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        x[2 * i] = bf16_bits_to_f32(raw[i] & 0xffffu);
+        x[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
+    }
+    return encode8_div(x, scale, rs, rs_ok);
 }
 
 __global__ __launch_bounds__(kQThreads) void q_encode_kernel(
@@ -69,18 +96,21 @@ __global__ __launch_bounds__(kQThreads) void q_encode_kernel(
         scale = m == 0.0f ? 1.0f : m / 448.0f;               // IEEE division
         if (blockIdx.x == 0 && threadIdx.x == 0) *q_scale = scale;
     }
+    // codes of fp32(q / scale), the IEEE quotient (encode8_div)
+    const float rs = 1.0f / scale;
+    const bool rs_ok = recip_ok(scale);
+    const u32x4 *qv = reinterpret_cast<const u32x4 *>(q);
+    u32x2 *ov = reinterpret_cast<u32x2 *>(q8);
+    const int64_t stride = (int64_t)gridDim.x * kQThreads;
     for (int64_t v = (int64_t)blockIdx.x * kQThreads + threadIdx.x; v < n_vec;
-         v += (int64_t)gridDim.x * kQThreads) {
-        const u32x4 raw = reinterpret_cast<const u32x4 *>(q)[v];
-        float y[8];
+         v += kQUnroll * stride) {
+        u32x4 raw[kQUnroll];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            y[2 * i] = bf16_bits_to_f32(raw[i] & 0xffffu) / scale;
-            y[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16) / scale;
-        }
-        u32x2 codes = {pack4_e4m3(y[0], y[1], y[2], y[3]),
-                       pack4_e4m3(y[4], y[5], y[6], y[7])};
-        reinterpret_cast<u32x2 *>(q8)[v] = codes;
+        for (int u = 0; u < kQUnroll; u++)
+            raw[u] = v + u * stride < n_vec ? qv[v + u * stride] : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < kQUnroll; u++)
+            if (v + u * stride < n_vec) ov[v + u * stride] = encode_vec(raw[u], scale, rs, rs_ok);
     }
 }
 

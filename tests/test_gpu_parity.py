@@ -107,6 +107,60 @@ def test_quantize_zero_tensor(orc):
     assert np.array_equal(G.host(q8), orc.q_quantize(q, np.float32(1.0)))
 
 
+def _quantize_scales():
+    """Divisors for the exhaustive encode test: powers of two (every quotient
+    exact, so many land exactly halfway between two codes), small multiples
+    of them, random log-uniform ones, and ones whose reciprocal is not a
+    normal number (the division-only path)."""
+    rng = np.random.default_rng(448)
+    s = [1.0, 0.37, 1.0 / 448.0, 2.0 ** -7, 2.0 ** 5, 3.0 * 2.0 ** -9, 5.0 * 2.0 ** 3,
+         7.0 / 448.0, 2.0 ** -125, 1e-40, 2.0 ** 125, 3e38]
+    s += list(np.exp2(rng.uniform(-30, 30, 40)))
+    return [np.float32(v) for v in s]
+
+
+def test_quantize_every_bf16_pattern_given_scales(orc):
+    """Every bf16 value (NaN, inf, subnormals, zeros of both signs included)
+    divided by each divisor and encoded, bit for bit: the kernel's product by
+    1/s with its exact fallback must give the codes of the IEEE quotient."""
+    q = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    qd = G.dev(q)
+    for sc in _quantize_scales():
+        q8, _ = G.run_quantize(qd, scale_given=sc)
+        ref = orc.q_quantize(q, sc)
+        got = G.host(q8)
+        bad = np.nonzero(got != ref)[0]
+        assert len(bad) == 0, (float(sc), len(bad), q[bad][:6], got[bad][:6], ref[bad][:6])
+
+
+def test_writer_scaled_every_bf16_magnitude(orc):
+    """528-byte writer over groups whose largest value is set, filled with
+    every finite bf16 pattern no larger than it, for several group maxima:
+    codes and scales bit for bit."""
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = (pats.astype(np.uint32) << 16).view(np.float32)
+    groups = []
+    for amax in [1.0, 448.0, 3.3e-3, 7.5, 2.0 ** -20, 1.7e5]:
+        a = np.float32(amax)
+        ok = pats[np.isfinite(vals) & (np.abs(vals) <= a)]
+        n = -(-len(ok) // 127) * 127
+        body = np.resize(ok, n).reshape(-1, 127)
+        head = np.full((body.shape[0], 1), W.bf16_bits(np.array([a], np.float32))[0], np.uint16)
+        groups.append(np.concatenate([head, body], axis=1))
+    g = np.concatenate(groups)
+    g = np.concatenate([g, g[: (-len(g)) % 4]])
+    kv = g.reshape(-1, 512)
+    n = kv.shape[0]
+    slots = np.arange(n, dtype=np.int64)
+    ref = np.zeros((n, 528), np.uint8)
+    assert orc.kv_write(kv, slots, ref, W.SCALED) == 0
+    pool = torch.zeros((n, 528), dtype=torch.uint8, device=G.DEV)
+    assert G.run_kv_write(kv, slots, pool, W.SCALED) == 0
+    got = G.host(pool)
+    bad = np.nonzero(got != ref)
+    assert len(bad[0]) == 0, (len(bad[0]), bad[0][:4], bad[1][:4])
+
+
 # ------------------------------------------------------------- attention
 
 def test_fp8_decode_exact_one_hot(orc):
