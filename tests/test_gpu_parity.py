@@ -266,6 +266,33 @@ def test_trailing_masked_entries(orc, layout, phase, H):
             assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
 
 
+@pytest.mark.parametrize("H", [16, 64])
+@pytest.mark.parametrize("layout", [W.RAW, W.SCALED], ids=["raw", "scaled"])
+def test_decode_more_units_than_cus(orc, layout, H):
+    """Decode with more (token, head block) units than compute units (so
+    workgroups run in several rounds, each split holding a whole row) and
+    ragged widths (every later entry -1), tokens of equal width spread over
+    the batch and a few rows empty."""
+    T, K = 300, 512
+    rng = np.random.default_rng(4000 + 10 * layout + H)
+    widths = rng.choice([0, 1, 63, 64, 65, 200, 383, 384, 511, 512], size=T)
+    wl = W.small(401 + layout, T=T, H=H, K=K, layout=layout, seq_len=700,
+                 page_size=64, neg_frac=0.0)
+    topk = wl.topk.copy()
+    for t in range(T):
+        topk[t, widths[t]:] = -1
+    wl = W.Workload(**{**wl.__dict__, "topk": topk})
+    pool = P.build_pool(orc, wl)
+    di = G.DevInputs(wl)
+    ref, ref_lse, ref_err = _oracle_attn(orc, wl, pool)
+    out, lse, err = G.run_attn(di, G.dev(pool), phase=0)
+    assert err == ref_err == 0
+    G.assert_attn_close(out, ref, where=f"{T} tokens, H {H}, layout {layout}")
+    G.assert_lse_close(lse, ref_lse)
+    for t in np.nonzero(widths == 0)[0]:
+        assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
+
+
 BF16_SMALL = [
     dict(seed=231, T=5, H=16, K=256, layout=W.BF16),
     dict(seed=232, T=3, H=8, K=384, layout=W.BF16, dup_frac=0.2, neg_frac=0.3),
