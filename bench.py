@@ -12,10 +12,14 @@ that at least 1 GiB of rows is gathered per rotation and the 256 MB
 Infinity Cache cannot serve the step from the previous visit.
 
 Prints ONE JSON line.  `value` is query tokens per second of the whole step
-loop; `roofline` relates the attention call's algorithmic bytes (decode:
-gathered row bytes) or FLOPs (prefill) to its duration measured with HIP
-events on the launch stream (on every eighth timed step); `cpu_baseline`
-times the CPU oracle on a bounded sample of the same workload.
+loop (W warm-up steps, then one untimed step per layer pool the warm-up did
+not reach, then K timed steps with nothing else on the stream).  After the
+timed loop, a timing pass runs --timing-calls more steps (at least 20) in
+which the writer, the query cast and the attention call are each bracketed
+by HIP events on the launch stream; `roofline` relates the attention call's
+algorithmic bytes (decode: gathered row bytes) or FLOPs (prefill) to its mean
+duration there, and the median, p10 and p90 are reported beside it.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -35,7 +39,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_TFLOPS = 2500.0       # dense bf16/f16 matrix peak, published
 MFMA_FP8_TFLOPS = 5000.0        # dense fp8 matrix peak, published
 METRIC = "query tok/s + gathered-KV GB/s (% HBM peak), decode H=16 top-k=2048"
-EV_EVERY = 8                    # timed steps per event-timed attention call
+MIN_TIMING_CALLS = 20           # event-timed attention calls, at least
 
 
 class TimingEvent:
@@ -109,6 +113,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (counter scaling)")
+    ap.add_argument("--timing-calls", type=int, default=200,
+                    help="event-timed steps after the timed loop (at least 20)")
     ap.add_argument("--op", default="attention", choices=["attention", "transform"],
                     help="transform: time the index transform alone on the "
                          "workload's top-k rows (page table -> compacted slots)")
@@ -141,6 +147,9 @@ def main():
 
     valid_entries = int(np.sum(wl.topk >= 0))
     gathered = valid_entries * R                       # algorithmic bytes / call
+    # the same with each token's repeated entries counted once
+    unique_entries = int(sum(np.unique(r[r >= 0]).size for r in wl.topk))
+    unique_gathered = unique_entries * R
     flops = 4.0 * H * 512 * valid_entries              # QK + PV per call
     if args.layers > 0:
         layers = args.layers
@@ -195,12 +204,19 @@ def main():
     attn = dsa.dsa_sparse_attn_prefill if prefill else dsa.dsa_sparse_attn_decode
 
     def step(i, ev=None):
+        """One pass of the hot path on layer pool i % layers; `ev` (four
+        timing events) brackets the writer, the query cast and the attention
+        call."""
         layer = i % layers
         pool = pools[layer]
+        if ev is not None:
+            ev[0].record()
         if n_new:
             dsa.check(dsa.dsa_kv_write(kv_new, n_new, 512 + rope, dsa.DSA_BF16, 512, rope,
                                        slot_map, pool, wl.num_slots, wl.layout,
                                        dsa.DSA_FP8_E4M3FN))
+        if ev is not None:
+            ev[1].record()
         if prefill:
             dsa.check(dsa.dsa_quantize_q_fp8(qs[layer], T * H * 512, dsa.DSA_BF16,
                                              q8, q_scale, 0, dsa.DSA_FP8_E4M3FN,
@@ -209,34 +225,46 @@ def main():
         else:
             q, qd, qsc = qs[layer], dsa.DSA_BF16, None
         if ev is not None:
-            ev[0].record()
+            ev[2].record()
         dsa.check(attn(q, qd, qsc, T, H, 512, rope, pool, wl.num_slots, wl.layout,
                        dsa.DSA_FP8_E4M3FN, topk, K, pt, wl.page_size, max_pages,
                        num_seqs, ts, sl, wl.softmax_scale, out, out_dtype, lse,
                        ws, wsb, None))
         if ev is not None:
-            ev[1].record()
+            ev[3].record()
 
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    # the attention call of every EV_EVERY-th timed step is bracketed by
-    # timing events, which would otherwise add their own cost to every
-    # step's throughput
-    sampled = list(range(0, args.steps, EV_EVERY))
-    events = {i: (TimingEvent(), TimingEvent())
-              for i in sampled}
+    # every layer pool meets the kernels once before the timed loop, whatever
+    # the warm-up count (first touches of a pool cost page-table walks)
+    pool_warm = list(range(args.warmup, layers))
+    for i in pool_warm:
+        step(i)
+    first = max(args.warmup, layers)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, events.get(i))
+        step(first + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    attn_ms = [a.elapsed_time(b) for a, b in events.values()]
-    attn_avg_s = float(np.mean(attn_ms)) * 1e-3
     tok_s = T * args.steps / elapsed
+
+    # timing pass: the same steps, continuing the pool rotation, with the
+    # writer, the query cast and the attention call each bracketed by events
+    # (a pair of events costs the stream time of its own, so the throughput
+    # loop above carries none)
+    n_ev = max(MIN_TIMING_CALLS, args.timing_calls)
+    events = [tuple(TimingEvent() for _ in range(4)) for _ in range(n_ev)]
+    torch.cuda.synchronize()
+    for j in range(n_ev):
+        step(first + args.steps + j, events[j])
+    torch.cuda.synchronize()
+    writer_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    qcast_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    attn_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+    attn_avg_s = float(np.mean(attn_ms)) * 1e-3
 
     traffic = committed_traffic(wl.name)
     if prefill:
@@ -285,11 +313,19 @@ def main():
             "out": args.out_dtype, "layer_pools": layers,
         },
         "attn_us": attn_avg_s * 1e6,
-        "attn_timed_calls": len(attn_ms),
+        "attn_us_median": float(np.median(attn_ms)) * 1e3,
         "attn_us_p10_p90": [float(np.percentile(attn_ms, 10)) * 1e3,
                             float(np.percentile(attn_ms, 90)) * 1e3],
+        "attn_timed_calls": int(len(attn_ms)),
+        "attn_tok_s": T / attn_avg_s,
+        "writer_us": float(np.mean(writer_ms)) * 1e3 if n_new else None,
+        "writer_rows": n_new,
+        "q_cast_us": float(np.mean(qcast_ms)) * 1e3 if prefill else None,
+        "pool_warm_calls": len(pool_warm),
         "gathered_GBps": gathered / attn_avg_s / 1e9,
         "gathered_bytes_per_call": gathered,
+        "unique_gathered_bytes_per_call": unique_gathered,
+        "unique_gathered_GBps": unique_gathered / attn_avg_s / 1e9,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -319,20 +355,20 @@ def bench_transform(args, wl, dev):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    sampled = set(range(0, args.steps, EV_EVERY))
-    events = {i: (TimingEvent(), TimingEvent())
-              for i in sampled}
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ev = events.get(i)
-        if ev:
-            ev[0].record()
         call()
-        if ev:
-            ev[1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    call_s = float(np.mean([a.elapsed_time(b) for a, b in events.values()])) * 1e-3
+    n_ev = max(MIN_TIMING_CALLS, args.timing_calls)
+    events = [(TimingEvent(), TimingEvent()) for _ in range(n_ev)]
+    for ev in events:
+        ev[0].record()
+        call()
+        ev[1].record()
+    torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(b) for a, b in events])
+    call_s = float(np.mean(call_ms)) * 1e-3
     nbytes = 4 * T * K + 4 * T * K + 4 * T
     achieved = nbytes / call_s / 1e9
     rec = {
@@ -346,6 +382,8 @@ def bench_transform(args, wl, dev):
         "config": {"workload": f"topk_transform/{wl.name}", "T": T, "k_in": K, "k_out": K,
                    "page_size": wl.page_size},
         "transform_us": call_s * 1e6,
+        "transform_us_median": float(np.median(call_ms)) * 1e3,
+        "transform_timed_calls": int(len(call_ms)),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": committed_traffic(wl.name, "topk_transform",
@@ -363,7 +401,8 @@ def bench_transform(args, wl, dev):
             n += 1
         rec["cpu_baseline"] = {"value": T * K * n / (time.perf_counter() - t0),
                                "unit": "entries/s", "cores": 1, "kind": "oracle",
-                               "sample": f"{n} whole transform(s) of the {wl.name} rows"}
+                               "sample": f"{n} whole transform(s) of the {wl.name} rows",
+                               **host_description()}
     print(json.dumps(rec), flush=True)
 
 
@@ -391,6 +430,22 @@ def committed_traffic(workload, op="attn", source="attn.hip"):
     if fields.get("kernel_source_sha256") != h.hexdigest():
         return None
     return float(fields["traffic_bytes_per_call"])
+
+
+def host_description():
+    """The host the oracle runs on: logical CPUs of the machine and of this
+    process, and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"nproc": avail, "machine_cpus": os.cpu_count(), "cpu_model": model}
 
 
 def cpu_baseline(wl, budget_s):
@@ -440,7 +495,7 @@ def cpu_baseline(wl, budget_s):
         if t_total >= budget_s or steps >= 500:
             break
     return {"value": tokens / t_total, "unit": "tok/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", **host_description(),
             "sample": f"{steps} step(s) of {wl.name}: writer on the "
                       f"{0 if wl.kv_new is None else wl.kv_new.shape[0]} "
                       f"new rows + FP64 attention for {T_s} tokens x {wl.H} heads x "

@@ -43,9 +43,12 @@
  * Conventions for every entry point:
  *   - Pointers are device pointers unless stated otherwise.  The caller owns
  *     every buffer; the library allocates nothing and keeps no state beyond a
- *     once-per-device architecture check.
- *   - All argument checks run on the host before any HIP call and return a
- *     status; nothing is launched unless the status is DSA_OK.  Values stored
+ *     once-per-device architecture and compute-unit query.
+ *   - All argument checks run on the host before any launch and return a
+ *     status; nothing is launched unless the status is DSA_OK (the pages
+ *     reject unsupported formats and widths "before kernel dispatch" [RAW,
+ *     Modifications]).  The only device query is the once-per-device
+ *     architecture and compute-unit lookup.  Values stored
  *     in device memory (indices, slots, sequence ids) are data: invalid ones
  *     are masked on the device and counted into *err_count (optional int32
  *     device counter that is only ever incremented; the caller zeroes it).
@@ -83,6 +86,11 @@ typedef enum dsa_dtype {
     DSA_FP8_E4M3FNUZ = 3
 } dsa_dtype;
 
+/* Status codes.  Each rejection is returned before anything is launched:
+ * the pages require unsupported FP8 flavours (E4M3FNUZ), latent widths other
+ * than the rows' and unknown layouts to be refused before kernel dispatch
+ * [RAW, Modifications], and the geometry to be checked as required integers
+ * against the layout [Q8, review thread]. */
 typedef enum dsa_status {
     DSA_OK = 0,
     DSA_ERR_NULL = 1,           /* a required pointer is NULL                 */
@@ -102,7 +110,9 @@ typedef enum dsa_status {
  * tested surface.] */
 int32_t dsa_kv_row_bytes(int32_t layout);
 
-/* Static, NUL-terminated name of a status code ("DSA_OK", ...). */
+/* Static, NUL-terminated name of a status code ("DSA_OK", ...;
+ * "DSA_ERR_UNKNOWN" for a value outside the enum): the message of the
+ * before-dispatch rejections [RAW, Modifications]. */
 const char *dsa_status_string(int32_t status);
 
 /*
@@ -146,7 +156,10 @@ int32_t dsa_kv_write(const void *kv, int64_t n, int64_t kv_row_stride,
  *   q_scale   one fp32 in device memory.  scale_given == 0: written with
  *             fp32(amax|q| / 448) (1 when amax = 0).  scale_given != 0: read.
  *   workspace dsa_quantize_q_workspace_bytes(n_elems) bytes (partial maxima);
- *             NULL allowed when that is 0 or scale_given != 0.
+ *             NULL allowed when that is 0 or scale_given != 0.  The caller
+ *             provides this bounded scratch, so the call neither allocates
+ *             nor synchronises [SCALED, Modifications: bounded workspace, no
+ *             host sync].
  * Codes are E4M3(fp32(q / q_scale)), round to nearest even, saturating.
  * n_elems must be a multiple of 8.  n_elems == 0 is a no-op.
  */
@@ -154,6 +167,9 @@ int32_t dsa_quantize_q_fp8(const void *q, int64_t n_elems, int32_t q_dtype,
                            void *q8, float *q_scale, int32_t scale_given,
                            int32_t fp8_format, void *workspace,
                            size_t workspace_bytes, void *stream);
+/* Bytes of the quantize workspace for n_elems values: 4 per block of the
+ * amax pass (a pure function of n_elems; 0 for n_elems <= 0) [SCALED,
+ * Modifications: a bounded workspace sized from the shape]. */
 size_t dsa_quantize_q_workspace_bytes(int64_t n_elems);
 
 /*
@@ -216,7 +232,12 @@ int32_t dsa_sparse_attn_prefill(
     void *workspace, size_t workspace_bytes, int32_t *err_count, void *stream);
 
 /* Workspace bytes the attention call needs for this shape and phase
- * (0 = decode, 1 = prefill); a pure function of its arguments. */
+ * (0 = decode, 1 = prefill): the fp32 split partials of the decode, whose
+ * split count fills the current device's compute units (256 are assumed when
+ * no device can be queried); 0 when the call needs none.  The caller owns
+ * this bounded scratch, so the attention neither allocates nor synchronises
+ * [SCALED, Modifications: selected rows go through a bounded workspace, with
+ * no host sync]. */
 size_t dsa_attn_workspace_bytes(int32_t T, int32_t H, int32_t K, int32_t phase);
 
 /*

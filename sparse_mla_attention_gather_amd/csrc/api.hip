@@ -1,13 +1,14 @@
 // api.hip -- the C ABI declared in include/dsa.h: argument validation (all of
-// it on the host, before any HIP call), the once-per-device architecture
-// check, and dispatch to the launchers.
+// it on the host, before any launch), the once-per-device architecture and
+// compute-unit query, and dispatch to the launchers.
 //
 // Rejections follow the SGLang pages: a latent width other than the rows'
 // 512 and E4M3FNUZ are refused before any kernel is dispatched ("extend CUDA
 // TileLang raw FP8 KV path", Modifications); the geometry is passed as
-// required integers and checked, not inferred from a model name, and a
-// nonzero RoPE width (the 656-byte layout) is refused ("[DSA] Support
-// flashmla_sparse_q8 prefill backend on CUDA", review thread).
+// required integers and checked against the row layout, not inferred from a
+// model name ("[DSA] Support flashmla_sparse_q8 prefill backend on CUDA",
+// review thread): the RoPE width must be the layout's own (64 for the
+// 656-byte rows, 0 for every other layout).
 #include <atomic>
 #include <cstring>
 
@@ -17,23 +18,42 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
+constexpr int kDefaultCus = 256;             // MI355X: 8 XCDs x 32 compute units
 std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_cus[kMaxDevices];         // compute units (set with the state)
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+// Architecture and compute-unit count of device `dev`, queried once.
+int device_state(int dev) {
+    int st = g_arch_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+        g_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : kDefaultCus,
+                         std::memory_order_relaxed);
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_state[dev].store(st, std::memory_order_release);
+    }
+    return st;
+}
 
 int32_t check_device() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return DSA_ERR_DEVICE;
-    int st = g_arch_state[dev].load(std::memory_order_acquire);
-    if (st == 0) {
-        hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DSA_ERR_DEVICE;
-        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-        g_arch_state[dev].store(st, std::memory_order_release);
-    }
-    return st == 1 ? DSA_OK : DSA_ERR_DEVICE;
+    return device_state(dev) == 1 ? DSA_OK : DSA_ERR_DEVICE;
+}
+
+// Compute units the decode split count is sized for: those of the current
+// device, or 256 (an MI355X) when no device can be queried, so that the
+// workspace size is defined on a host without a GPU as well.
+int split_target_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kDefaultCus;
+    if (device_state(dev) == 0) return kDefaultCus;
+    return g_cus[dev].load(std::memory_order_relaxed);
 }
 
 int32_t check_fp8_format(int32_t f) {
@@ -84,7 +104,7 @@ int32_t validate_attn(const void *q, int32_t q_dtype, const float *q_scale,
     if (!q || !pool || !topk || !out) return DSA_ERR_NULL;
     if (q_dtype == DSA_FP8_E4M3FN && !q_scale) return DSA_ERR_NULL;
     if (!aligned16(q) || !aligned16(pool) || !aligned16(out)) return DSA_ERR_ALIGN;
-    const size_t need = dsa::attn_workspace_bytes(T, H, K, phase);
+    const size_t need = dsa::attn_workspace_bytes(T, H, K, phase, split_target_cus());
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
         if (!aligned256(workspace)) return DSA_ERR_ALIGN;
@@ -131,7 +151,7 @@ int32_t run_attn(int32_t phase, const void *q, int32_t q_dtype,
     a.out = out;
     a.lse = lse;
     a.ws = static_cast<float *>(workspace);
-    a.n_splits = dsa::attn_splits(T, H, K, phase, layout);
+    a.n_splits = dsa::attn_splits(T, H, K, phase, layout, split_target_cus());
     a.split_len = 0;
     a.err_count = err_count;
     hipError_t e = dsa::launch_attn(a, layout, q_dtype == DSA_FP8_E4M3FN,
@@ -266,7 +286,7 @@ int32_t dsa_topk_transform(const int32_t *topk, int32_t T, int32_t k_in,
 
 size_t dsa_attn_workspace_bytes(int32_t T, int32_t H, int32_t K, int32_t phase) {
     if (T <= 0 || H <= 0 || K <= 0 || K % 128 != 0) return 0;
-    return dsa::attn_workspace_bytes(T, H, K, phase);
+    return dsa::attn_workspace_bytes(T, H, K, phase, split_target_cus());
 }
 
 int32_t dsa_sparse_attn_decode(

@@ -70,10 +70,6 @@
 #include "common.h"
 #include "launch.h"
 
-#ifndef DSA_DECODE_TARGET_BLOCKS
-#define DSA_DECODE_TARGET_BLOCKS 256
-#endif
-
 namespace dsa {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -105,18 +101,26 @@ struct Lds {
     static constexpr int kParts = 2;                             // QK dim parts
     static constexpr int kRowPitch = LAYOUT == 3 ? 1024 : 512;   // LDS bytes per row
     static constexpr int kBufBytes = kTile * kRowPitch;          // 32 KB (bf16 rows: 64 KB)
+    static constexpr bool kHasScales = LAYOUT == 1 || LAYOUT == 2;
+    // raw FP8 rows in 16-head blocks carry P to the PV product as two f16
+    // terms (hi + lo), see the softmax
+    static constexpr bool kLo = LAYOUT == 0 && NT == 1;
     static constexpr int kScBytes = kTile * 16;                  // 1 KB scales
     static constexpr int kRopeTile = kTile * 2 * kRopeDim;       // 8 KB RoPE parts
     static constexpr int kOffScales = kNB * kBufBytes;
-    static constexpr int kOffSlots = kOffScales + kNScale * kScBytes;
+    static constexpr int kOffSlots = kOffScales + (kHasScales ? kNScale * kScBytes : 0);
     // partial S^T of the waves holding dim parts 1.. (16 x 16 fp32 each)
     static constexpr int kOffSp = kOffSlots + kMaxSplit * 4;
     static constexpr int kSpBytes = NT * (kParts - 1) * 4 * 1024;
-    // P ([kHB][64] f16, swizzled) and the quarter maxima ([kHB][4] fp32),
-    // two of each (by tile parity)
+    // P ([kHB][64] 16-bit, swizzled; the lo terms follow the hi terms): one
+    // buffer, since the PV waves hold tile k's P in registers before the
+    // barrier after which the owners write tile k+1's; then the quarter
+    // maxima ([kHB][4] fp32), two (by tile parity: each owner reads the
+    // previous tile's while it writes its own)
     static constexpr int kOffP = kOffSp + kSpBytes;
     static constexpr int kPBytes = kHB * kTile * 2;
-    static constexpr int kOffMq = kOffP + 2 * kPBytes;
+    static constexpr int kPArea = (kLo ? 2 : 1) * kPBytes;
+    static constexpr int kOffMq = kOffP + kPArea;
     static constexpr int kMqBytes = kHB * 16;
     static constexpr int kOffRedL = kOffMq + 2 * kMqBytes;       // [kHB][4] fp32
     // group-scaled rows: running largest scale of each 128-wide group (the
@@ -132,7 +136,7 @@ struct Lds {
     static constexpr int kOffRope = kOffFac + (LAYOUT == 1 || LAYOUT == 2 ? 2 * kFacBytes : 0);
     static constexpr int kBytes = kOffRope + (LAYOUT == 2 ? kNB * kRopeTile : 0);
     // the token's page-table row is staged over the sp and P areas
-    static constexpr int kPtPer = (kSpBytes + 2 * kPBytes) / 4 / kThreads;
+    static constexpr int kPtPer = (kSpBytes + kPArea) / 4 / kThreads;
     static_assert(kBytes <= 160 * 1024, "LDS budget");
     static_assert(kOffRope % 16 == 0 && kOffScales % 16 == 0, "16-byte DMA destinations");
     static_assert(kPtPer >= 1, "page-table staging");
@@ -266,16 +270,20 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, uint32_t lds0, con
                              : LAYOUT == 2 ? kRopeRowBytes : kBf16RowBytes;
     const int r0 = kRowsPerWave * w;
     const uint32_t dst = lds0 + buf * L::kBufBytes + r0 * L::kRowPitch;
+    // A masked entry (slot < 0) reads zero row r of kZeroRow instead.  The
+    // source is one selected base plus one offset, so that the compiler has
+    // no per-lane 64-bit zero-row address to keep live across the tile loop.
+    auto src_of = [&](int32_t slot, int r, int byte) {
+        const uint8_t *base = slot >= 0 ? a.pool : kZeroRow;
+        return base + (int64_t)(slot >= 0 ? slot : r) * kRow + byte;
+    };
     if constexpr (LAYOUT == 3) {
         // one 1024-byte row per instruction: lane l -> position l, holding
         // chunk l ^ swz(row)
 #pragma unroll
         for (int k = 0; k < kRowsPerWave; k++) {
             const int r = r0 + k;
-            const int chunk = lane ^ swz(r);
-            const uint8_t *src = s.r4[k] >= 0 ? a.pool + (int64_t)s.r4[k] * kRow + chunk * 16
-                                              : kZeroRow + r * kRow + chunk * 16;
-            dma16(src, dst + k * 1024);
+            dma16(src_of(s.r4[k], r, (lane ^ swz(r)) * 16), dst + k * 1024);
         }
         return;
     }
@@ -283,26 +291,17 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, uint32_t lds0, con
 #pragma unroll
     for (int k = 0; k < kLoadsRaw; k++) {
         const int r = r0 + 2 * k + (lane >> 5);
-        const int chunk = pos ^ swz(r);
-        const uint8_t *src = s.row[k] >= 0 ? a.pool + (int64_t)s.row[k] * kRow + chunk * 16
-                                           : kZeroRow + r * kRow + chunk * 16;
-        dma16(src, dst + k * 1024);
+        dma16(src_of(s.row[k], r, (pos ^ swz(r)) * 16), dst + k * 1024);
     }
     if (LAYOUT == 1 || LAYOUT == 2) {
-        if (lane < kRowsPerWave) {
-            const int r = r0 + lane;
-            const uint8_t *src = s.sc >= 0 ? a.pool + (int64_t)s.sc * kRow + kD
-                                           : kZeroRow + r * kRow + kD;
-            dma16(src, lds0 + L::kOffScales + sbuf * L::kScBytes + r0 * 16);
-        }
+        if (lane < kRowsPerWave)
+            dma16(src_of(s.sc, r0 + lane, kD), lds0 + L::kOffScales + sbuf * L::kScBytes + r0 * 16);
     }
     if (LAYOUT == 2) {
         if (lane < 8 * kRowsPerWave) {
             const int r = r0 + (lane >> 3);
-            const int chunk = (lane & 7) ^ swz(r);
-            const uint8_t *src = s.rp >= 0 ? a.pool + (int64_t)s.rp * kRow + kScaledBytes + chunk * 16
-                                           : kZeroRow + r * kRow + kScaledBytes + chunk * 16;
-            dma16(src, lds0 + L::kOffRope + buf * L::kRopeTile + r0 * 2 * kRopeDim);
+            dma16(src_of(s.rp, r, kScaledBytes + ((lane & 7) ^ swz(r)) * 16),
+                  lds0 + L::kOffRope + buf * L::kRopeTile + r0 * 2 * kRopeDim);
         }
     }
 }
@@ -319,35 +318,26 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     constexpr int kGpp = kDP / 128;              // scale groups per part
     constexpr int kChunks = kDP / 16;            // 16-byte row chunks per part
     constexpr int kXc = LAYOUT == 3 ? kDP / 32 : kDP / 64;   // of which one lane holds (4 lane groups)
-    // Schedule.  Pipelined: waves 0-7 score (QK and the owners' softmax),
-    // waves 8-15 accumulate PV one tile behind, so the owners' softmax of
-    // tile k overlaps the PV of tile k-1 and each tile's operand reads
-    // overlap the phase before.  Sequential (kept for comparison, with
-    // DSA_SEQUENTIAL for 32-head blocks): every wave scores and accumulates,
-    // each tile read, scored, normalised and accumulated in turn.
-#ifdef DSA_SEQUENTIAL
-    constexpr bool kPipe = NT == 1;
-#else
-    constexpr bool kPipe = true;
-#endif
+    // Schedule: waves 0-7 score (QK and the owners' softmax), waves 8-15
+    // accumulate PV one tile behind, so the owners' softmax of tile k
+    // overlaps the PV of tile k-1 and each tile's operand reads overlap the
+    // phase before.
     static_assert(kParts == 2, "one publishing wave per head tile and quarter");
     // PV operands read in their own step (one register set; a tile's buffer
     // is refilled right after its step): 32-head blocks and 656-byte rows,
     // whose extra operands would not fit otherwise
-    constexpr bool kLate = kPipe && (NT == 2 || LAYOUT >= 2);
+    constexpr bool kLate = NT == 2 || LAYOUT >= 2;
     constexpr bool kScaled = LAYOUT == 1 || LAYOUT == 2;   // rows carry group scales
-    constexpr int kDT = kPipe ? 4 : 2;           // PV: 16-dim tiles per wave
-#ifndef DSA_FILL0
-#define DSA_FILL0 2
-#endif
-    constexpr int kFill0 = DSA_FILL0;            // tiles requested before the first lands
+    constexpr int kDT = 4;                       // PV: 16-dim tiles per wave
+    // tiles requested before the first lands (1 to 4 measured the same)
+    constexpr int kFill0 = 2;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int kLoads = LAYOUT == 3 ? kRowsPerWave
                                        : kLoadsRaw + (kScaled ? 1 : 0) + (LAYOUT == 2 ? 1 : 0);
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
-    const bool is_v = kPipe && w >= 8;           // pipelined: a PV-only wave
+    const bool is_v = w >= 8;                    // a PV-only wave
     // Scoring (partials of 16 entries x 16 heads x one 256-dim part dp;
     // entry quarter q and head tile ht are owned -- parts added, P formed --
     // by one wave, to which the wave holding the other part publishes its
@@ -360,22 +350,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     //   32 heads, bf16 query (kRowPair: the query of both head tiles would
     //     not fit the 128 registers a lane has at 16 waves per CU): wave
     //     (rh = w & 1, dp = (w >> 1) & 1, ht = w >> 2) scores quarters 2rh
-    //     and 2rh + 1 of head tile ht and owns quarter 2rh + dp;
-    //   sequential: wave w scores quarter w & 3 of head tile (w >> 2) /
-    //     kParts, and the dp = 0 waves own it.
-    constexpr bool kRowPair = kPipe && NT == 2 && !QFP8;
+    //     and 2rh + 1 of head tile ht and owns quarter 2rh + dp.
+    constexpr bool kRowPair = NT == 2 && !QFP8;
     // scoring waves read a tile's row chunks in the tile's own step rather
     // than during the softmax before (possible with kLate's buffer rotation)
-    constexpr bool kOwnStep = kRowPair || (kPipe && LAYOUT >= 2);
+    constexpr bool kOwnStep = kRowPair || LAYOUT >= 2;
     constexpr int kRT = kRowPair ? 2 : 1;        // entry quarters a scoring wave scores
-    constexpr int kQT = kRowPair ? 1 : (kPipe ? NT : 1);   // head tiles it scores
+    constexpr int kQT = kRowPair ? 1 : NT;       // head tiles it scores
     const int rh = w & 1;
     const int dp = kRowPair ? (w >> 1) & 1 : (w >> 2) % kParts;      // QK: dims part
     const int wq = kRowPair ? 2 * rh + dp : w & 3;   // entry quarter owned (and scored)
-    const int ht = kRowPair ? (w >> 2) & 1
-                            : (kPipe ? (NT == 1 ? 0 : dp) : (w >> 2) / kParts);
-    const bool owner = !is_v && (kRowPair || (kPipe ? (NT == 1 ? dp == 0 : true) : dp == 0));
-    const int dbase = kPipe ? 64 * (w - 8) : 32 * w;   // PV: first of this wave's dims
+    const int ht = kRowPair ? (w >> 2) & 1 : (NT == 1 ? 0 : dp);
+    const bool owner = !is_v && (kRowPair || NT == 2 || dp == 0);
+    const int dbase = 64 * (w - 8);              // PV: first of this wave's dims
     const int n_hb = (a.H + kHB - 1) / kHB;
 
     // XCD-aware numbering: all of token t's workgroups are 8k + (t % 8)
@@ -414,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     if (!is_v) {
 #pragma unroll
         for (int nt = 0; nt < kQT; nt++) {
-            const int h = hb * kHB + ((kPipe && !kRowPair) ? nt : ht) * 16 + c;
+            const int h = hb * kHB + (kRowPair ? ht : nt) * 16 + c;
             const int64_t qrow = ((int64_t)t * a.H + (h < a.H ? h : 0)) * kQRow;
             if constexpr (LAYOUT == 2)
                 bqr = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
@@ -545,9 +532,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     float m_ref[NT];
     float s_run = 0.0f, s_ref = 0.0f;
     f32x4 acc[kDT][NT];
+    // One-term f16 P (raw rows in 32-head blocks, group-scaled rows): PV
+    // wave 8 accumulates the denominator itself, as the product of a ones
+    // operand with the very P operand of the numerator (same roundings,
+    // same rescales), so that the rounding of an entry's weight moves
+    // numerator and denominator alike.  (bf16 rows, whose kernel has no
+    // register to spare for it, sum the rounded P in the owners.)
+    constexpr bool kLacc = !L::kLo && LAYOUT != 3;
+    f32x4 lacc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) {
         m_ref[nt] = kNoMax;
+        lacc[nt] = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int dt = 0; dt < kDT; dt++) acc[dt][nt] = f32x4{0, 0, 0, 0};
     }
@@ -557,7 +553,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     u32x4 xc[kRT][kXc];
     u32x4 xcr;                  // 656-byte rows: this lane's RoPE chunk
     // (bf16 rows: eight 16-bit values per operand, u32x4)
-    std::conditional_t<LAYOUT == 3, u32x4, u32x2> tv[kPipe && !kLate ? 2 : 1][2][kDT];
+    std::conditional_t<LAYOUT == 3, u32x4, u32x2> tv[kLate ? 1 : 2][2][kDT];
     f32x4 part[kRT * kQT];      // [entry quarter][head tile]
 
     // Wait until this wave's DMA of tile j has landed: `issued` is the last
@@ -731,7 +727,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         for (int rt = 0; rt < kRT; rt++)
 #pragma unroll
             for (int nt = 0; nt < kQT; nt++) {
-                const int qt = (kPipe && !kRowPair) ? nt : ht;   // its head tile
+                const int qt = kRowPair ? ht : nt;         // its head tile
                 const int qq = kRowPair ? 2 * rh + rt : wq;        // its entry quarter
                 if (!(owner && qt == ht && qq == wq)) {
                     const int slot = qt * 4 + qq;
@@ -751,7 +747,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     auto softmax = [&](int j, auto then) {
         const int par = j & 1;
         float *mq_w = reinterpret_cast<float *>(lds + L::kOffMq + par * L::kMqBytes);
-        uint8_t *p_w = lds + L::kOffP + par * L::kPBytes;
+        uint8_t *p_w = lds + L::kOffP;
         const int hh = ht * 16 + c;
         const int4 sl4 = *reinterpret_cast<const int4 *>(slots + j * kTile + 16 * wq + 4 * g);
         // own part of the owned (quarter, head tile) plus the other part's,
@@ -795,21 +791,40 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         if (g == 0) lds[L::kOffFlags + par * kHB * 4 + hh * 4 + wq] = j > 0 && !moved;
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            p[i] = __builtin_amdgcn_exp2f(sv[i] - m_own);   // masked: 2^-inf = 0
-            l_part += p[i];
-        }
-        u32x2 pk;
+        for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_own);   // masked: 2^-inf = 0
+        // P goes to the PV product as 16-bit values.  Raw FP8 rows (whose
+        // values reach +-448) in 16-head blocks carry it as two f16 terms,
+        // hi = f16(P) and lo = f16(P - hi): one f16 rounding alone (2^-11
+        // relative) moves a weighted sum of such values by up to 2^-10 of
+        // its spread; the owners' shares of the denominator are then sums
+        // of P itself.  Everything else carries one term (f16; bf16 for
+        // bf16 rows, whose PV product takes bf16): in 32-head blocks a
+        // second term would double the PV waves' matrix work, which sets
+        // their pace.  The denominator of one-term P is formed from the
+        // operand itself in the PV waves (lacc); bf16 rows sum it here as
+        // rounded.
+        const int poff = p_off(hh, 2 * wq + (g >> 1)) + (g & 1) * 8;
         if constexpr (LAYOUT == 3) {
-            // bf16 rows multiply P as bf16 (the PV MFMA takes one type)
-            pk = u32x2{f32_to_bf16_bits(p[0]) | (f32_to_bf16_bits(p[1]) << 16),
-                       f32_to_bf16_bits(p[2]) | (f32_to_bf16_bits(p[3]) << 16)};
+            uint32_t b[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                b[i] = f32_to_bf16_bits(p[i]);
+                l_part += bf16_bits_to_f32(b[i]);
+            }
+            *reinterpret_cast<u32x2 *>(p_w + poff) = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
         } else {
             const f16x2 p01 = {(_Float16)p[0], (_Float16)p[1]};
             const f16x2 p23 = {(_Float16)p[2], (_Float16)p[3]};
-            pk = u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+            *reinterpret_cast<u32x2 *>(p_w + poff) =
+                u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+            if constexpr (L::kLo) {
+                const f16x2 l01 = {(_Float16)(p[0] - (float)p01[0]), (_Float16)(p[1] - (float)p01[1])};
+                const f16x2 l23 = {(_Float16)(p[2] - (float)p23[0]), (_Float16)(p[3] - (float)p23[1])};
+                *reinterpret_cast<u32x2 *>(p_w + L::kPBytes + poff) =
+                    u32x2{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
+                l_part += (p[0] + p[1]) + (p[2] + p[3]);
+            }
         }
-        *reinterpret_cast<u32x2 *>(p_w + p_off(hh, 2 * wq + (g >> 1)) + (g & 1) * 8) = pk;
         if (g == 0) mq_w[hh * 4 + wq] = m_own;
         if constexpr (kScaled) {
             // running largest scale of group wq (this tile's 64 entries one
@@ -824,7 +839,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             }
         }
     };
-    auto nothing = [] {};
 
     // O^T[dims dbase.., heads] += X^T . P^T over tile j's 64 entries from
     // tv[TPAR] and the P buffer of parity j & 1; P of quarter q weighted by
@@ -835,11 +849,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // pv_mma(TPAR, DT0, DT1) then accumulates dim tiles [DT0, DT1) from
     // tv[TPAR].  The pipelined schedule splits the dim tiles over its two
     // phases.
+    // P times a weight factor, formed in fp32 and rounded to f16 once
+    auto reweight_f16 = [](f16x8 &b, float f) {
+#pragma unroll
+        for (int e = 0; e < 8; e++) b[e] = (_Float16)((float)b[e] * f);
+    };
     f16x8 pv_bp[NT][2];
+    f16x8 pv_bl[L::kLo ? NT : 1][2];     // the lo terms (raw rows)
     auto pv_prep = [&](int j) {
         const int ppar = j & 1;
         const float *mq_lds = reinterpret_cast<const float *>(lds + L::kOffMq + ppar * L::kMqBytes);
-        const uint8_t *p_lds = lds + L::kOffP + ppar * L::kPBytes;
+        const uint8_t *p_lds = lds + L::kOffP;
         // While every quarter kept the previous reference (all four flags
         // set) the reference, O and P stay as they are.  Otherwise: m_ref
         // takes the largest quarter maximum (O rescaled when it moves) and
@@ -848,11 +868,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         // B operand P^T: entries ks*32 + g*8 + r of head nt*16 + c (one
         // 16-byte chunk, quarter 2ks + g/2); read together with the flags
         auto &bp = pv_bp;
+        auto &bl = pv_bl;
 #pragma unroll
         for (int nt = 0; nt < NT; nt++)
 #pragma unroll
-            for (int ks = 0; ks < 2; ks++)
+            for (int ks = 0; ks < 2; ks++) {
                 bp[nt][ks] = *reinterpret_cast<const f16x8 *>(p_lds + p_off(nt * 16 + c, 4 * ks + g));
+                if constexpr (L::kLo)
+                    bl[nt][ks] = *reinterpret_cast<const f16x8 *>(p_lds + L::kPBytes +
+                                                                 p_off(nt * 16 + c, 4 * ks + g));
+            }
         bool uneven = false;
 #pragma unroll
         for (int nt = 0; nt < NT; nt++)
@@ -879,11 +904,27 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             }
             if (__ballot(any_resc)) {
 #pragma unroll
-                for (int nt = 0; nt < NT; nt++)
+                for (int nt = 0; nt < NT; nt++) {
 #pragma unroll
                     for (int dt = 0; dt < kDT; dt++) acc[dt][nt] *= alpha[nt];
+                    if constexpr (kLacc) lacc[nt] *= alpha[nt];
+                }
             }
         }
+        // the denominator of one-term P from the operand as weighted
+        auto add_lacc = [&]() {
+            if constexpr (kLacc) {
+                if (w == 8) {
+#pragma unroll
+                    for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+                        for (int ks = 0; ks < 2; ks++) {
+                            const f16x8 one = {1, 1, 1, 1, 1, 1, 1, 1};
+                            lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(one, bp[nt][ks], lacc[nt], 0, 0, 0);
+                        }
+                }
+            }
+        };
         if constexpr (kScaled) {
             // the group's running largest scale (uniform): O moves to the
             // new reference when it grows; then P times each entry's factor
@@ -901,11 +942,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                     for (int dt = 0; dt < kDT; dt++) acc[dt][nt] *= beta;
                 s_ref = sr;
             }
+            if (reweight) {
+#pragma unroll
+                for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ks++) reweight_f16(bp[nt][ks], fq[nt][ks]);
+            }
+            add_lacc();
 #pragma unroll
             for (int nt = 0; nt < NT; nt++)
 #pragma unroll
-                for (int ks = 0; ks < 2; ks++)
-                    bp[nt][ks] *= reweight ? fk[ks] * (_Float16)fq[nt][ks] : fk[ks];
+                for (int ks = 0; ks < 2; ks++) bp[nt][ks] *= fk[ks];
+            return;
         } else if (reweight) {
 #pragma unroll
             for (int nt = 0; nt < NT; nt++)
@@ -921,11 +969,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                             b[e] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
                         }
                         bp[nt][ks] = __builtin_bit_cast(f16x8, b);
+                    } else if constexpr (L::kLo) {
+                        // hi + lo weighted in fp32 and split again
+#pragma unroll
+                        for (int e = 0; e < 8; e++) {
+                            const float v = ((float)bp[nt][ks][e] + (float)bl[nt][ks][e]) * fq[nt][ks];
+                            bp[nt][ks][e] = (_Float16)v;
+                            bl[nt][ks][e] = (_Float16)(v - (float)bp[nt][ks][e]);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                     } else {
-                        bp[nt][ks] *= (_Float16)fq[nt][ks];
+                        reweight_f16(bp[nt][ks], fq[nt][ks]);
                     }
                 }
         }
+        add_lacc();
     };
     auto pv_mma = [&](auto tpar, auto dt0, auto dt1) {
         constexpr int TPAR = decltype(tpar)::value;
@@ -943,13 +1001,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                         bv1, __builtin_bit_cast(bf16x8, pv_bp[nt][1]), acc[dt][nt], 0, 0, 0);
                 }
             } else {
-            const f16x8 av0 = e4m3x8_to_f16(tv[TPAR][0][dt][0], tv[TPAR][0][dt][1]);
-            const f16x8 av1 = e4m3x8_to_f16(tv[TPAR][1][dt][0], tv[TPAR][1][dt][1]);
+                const f16x8 av0 = e4m3x8_to_f16(tv[TPAR][0][dt][0], tv[TPAR][0][dt][1]);
+                const f16x8 av1 = e4m3x8_to_f16(tv[TPAR][1][dt][0], tv[TPAR][1][dt][1]);
 #pragma unroll
-            for (int nt = 0; nt < NT; nt++) {
-                acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, pv_bp[nt][0], acc[dt][nt], 0, 0, 0);
-                acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, pv_bp[nt][1], acc[dt][nt], 0, 0, 0);
-            }
+                for (int nt = 0; nt < NT; nt++) {
+                    acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, pv_bp[nt][0], acc[dt][nt], 0, 0, 0);
+                    acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, pv_bp[nt][1], acc[dt][nt], 0, 0, 0);
+                    if constexpr (L::kLo) {
+                        acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, pv_bl[nt][0], acc[dt][nt], 0, 0, 0);
+                        acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, pv_bl[nt][1], acc[dt][nt], 0, 0, 0);
+                    }
+                }
             }
         }
     };
@@ -970,42 +1032,44 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     auto epilogue = [&](auto scoring) {
         const float *mq_fin = reinterpret_cast<const float *>(
             lds + L::kOffMq + ((n_tiles - 1) & 1) * L::kMqBytes);
-        if (owner) {
-            l_part = sum_over_g(l_part);
-            if (g == 0) rl_lds[(ht * 16 + c) * 4 + wq] = l_part;
+        if constexpr (!kLacc) {
+            if (owner) {
+                l_part = sum_over_g(l_part);
+                if (g == 0) rl_lds[(ht * 16 + c) * 4 + wq] = l_part;
+            }
+        } else if (!decltype(scoring)::value) {
+            if (w == 8 && g == 0) {
+#pragma unroll
+                for (int nt = 0; nt < NT; nt++) rl_lds[nt * 16 + c] = lacc[nt][0];
+            }
         }
         __syncthreads();
         if constexpr (decltype(scoring)::value) return;   // the PV waves hold O
-        const int w_first = kPipe ? 8 : 0;    // writes m, l and lse
+        const int w_first = 8;                // writes m, l and lse
 #pragma unroll
         for (int nt = 0; nt < NT; nt++) {
             const int hh = nt * 16 + c;
             const int h = hb * kHB + hh;
             if (h >= a.H) continue;
-            const f32x4 mq = *reinterpret_cast<const f32x4 *>(mq_fin + hh * 4);
-            const f32x4 lq = *reinterpret_cast<const f32x4 *>(rl_lds + hh * 4);
             float l_tot = 0.0f;
+            if constexpr (kLacc) {
+                l_tot = rl_lds[hh];
+            } else {
+                const f32x4 mq = *reinterpret_cast<const f32x4 *>(mq_fin + hh * 4);
+                const f32x4 lq = *reinterpret_cast<const f32x4 *>(rl_lds + hh * 4);
 #pragma unroll
-            for (int q = 0; q < 4; q++) l_tot += lq[q] * __builtin_amdgcn_exp2f(mq[q] - m_ref[nt]);
+                for (int q = 0; q < 4; q++) l_tot += lq[q] * __builtin_amdgcn_exp2f(mq[q] - m_ref[nt]);
+            }
             const int64_t th = (int64_t)t * a.H + h;
             if (SPLIT) {
-                // the split's normalised output o / l (raw rows: f16, whose
-                // range holds any average of E4M3 values; 528-byte rows:
-                // fp32), then (m, l)
+                // the split's normalised output o / l in fp32 (a raw row's
+                // values reach +-448, where f16 would round by up to 0.125),
+                // then (m, l)
                 const float inv = (l_tot > 0.0f ? 1.0f / l_tot : 0.0f) * (kScaled ? s_ref : 1.0f);
                 const int64_t po = (th * a.n_splits + split) * kD + dbase + 4 * g;
 #pragma unroll
-                for (int dt = 0; dt < kDT; dt++) {
-                    const f32x4 o = acc[dt][nt] * inv;
-                    if constexpr (LAYOUT == 0) {
-                        const f16x2 o01 = {(_Float16)o[0], (_Float16)o[1]};
-                        const f16x2 o23 = {(_Float16)o[2], (_Float16)o[3]};
-                        *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.ws) + po + dt * 16) =
-                            u32x2{__builtin_bit_cast(uint32_t, o01), __builtin_bit_cast(uint32_t, o23)};
-                    } else {
-                        *reinterpret_cast<f32x4 *>(a.ws + po + dt * 16) = o;
-                    }
-                }
+                for (int dt = 0; dt < kDT; dt++)
+                    *reinterpret_cast<f32x4 *>(a.ws + po + dt * 16) = acc[dt][nt] * inv;
                 if (w == w_first && g == 0) {
                     float *ml = a.ws + (int64_t)a.T * a.H * a.n_splits * kD +
                                 (th * a.n_splits + split) * 2;
@@ -1034,7 +1098,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    if constexpr (kPipe) {
+    {
         // Tile k (parity PAR = k & 1), its operands already in registers:
         //   scoring waves: QK(k) -> partials; PV waves: the first half of
         //   tile k-1's dims (P buffer PAR^1, tv[PAR^1]);  [tile k+1 landed]
@@ -1072,7 +1136,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             first_tile([&] { if constexpr (!kLate) read_tv(0, I0{}); });
             auto vstep = [&](int k, auto par) {
                 constexpr int PAR = decltype(par)::value;
-                const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + 1 + kAhead, n_tiles - 1) * kTile, w, lane);
                 // tv set of tiles k-1 and k+1 (kLate: the one set, tiles
                 // k-1 then k)
                 using TP = std::integral_constant<int, kLate ? 0 : PAR ^ 1>;
@@ -1087,7 +1150,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 else if (k + 1 < n_tiles) read_tv(k + 1, TP{});
                 wait_lgkm0();
                 barrier_raw();
-                refill(k, nsl);
+                refill(k, read_slots<LAYOUT>(slots, min(k + 1 + kAhead, n_tiles - 1) * kTile, w, lane));
             };
             for (int k = 0; k < n_tiles; k += 2) {
                 vstep(k, I0{});
@@ -1121,41 +1184,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             }
             epilogue(std::true_type{});
         }
-    } else {
-        // P and the quarter maxima alternate between two buffers by tile
-        // parity, so the owners can read the previous tile's maxima while
-        // they publish the current ones
-        for (int k = 0; k < n_tiles; k++) {
-            const bool refill = k + kNB < n_tiles;
-            const TileSlots nsl = read_slots<LAYOUT>(slots, min(k + kNB, n_tiles - 1) * kTile, w, lane);
-            wait_tile(k, k == 0 ? kFill0 - 1 : k + kNB - 1);
-            barrier_raw();
-            if (k == 0) fill_rest();
-            read_xc(k);
-            read_tv(k, I0{});
-            qk(k);
-            // partials published, every wave's operands of this tile are in
-            // registers: the buffer takes the tile kNBuf ahead
-            wait_lgkm0();
-            barrier_raw();
-            if (refill) issue_tile<LAYOUT, NT>(a, lds0, nsl, k % kNB, (k + kNB) % kNScale, w, lane);
-            if (owner) softmax(k, nothing);
-            wait_lgkm0();
-            barrier_raw();
-            pv(k, I0{});
-        }
-        epilogue(std::false_type{});
     }
-
 }
 // Merge of the split partial states: one wavefront per (token, head), each
 // lane owning 8 of the 512 dims.  A split holds its normalised output o_s
-// (f16 for raw rows, fp32 for 528-byte rows) and (m_s, l_s); the merge is
+// (fp32) and (m_s, l_s); the merge is
 // sum_s 2^(m_s - M) l_s o_s / sum_s 2^(m_s - M) l_s.  Splits are taken CH at
 // a time (CH <= 8, the whole merge for up to eight splits): every split's
 // state in a chunk is loaded before any of it is used, so a chunk costs one
 // memory latency; chunks are merged online.
-template <bool OUT_BF16, int CH, bool F16>
+template <bool OUT_BF16, int CH>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -1174,15 +1212,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
             const int s = s0 + k < ns ? s0 + k : 0;
             m[k] = ml[2 * s];
             l[k] = ml[2 * s + 1];
-            if constexpr (F16) {
-                const f16x8 h = *reinterpret_cast<const f16x8 *>(
-                    reinterpret_cast<const _Float16 *>(a.ws) + ob + (int64_t)s * kD);
-                v0[k] = __builtin_convertvector(h.lo, f32x4);
-                v1[k] = __builtin_convertvector(h.hi, f32x4);
-            } else {
-                v0[k] = *reinterpret_cast<const f32x4 *>(a.ws + ob + (int64_t)s * kD);
-                v1[k] = *reinterpret_cast<const f32x4 *>(a.ws + ob + (int64_t)s * kD + 4);
-            }
+            v0[k] = *reinterpret_cast<const f32x4 *>(a.ws + ob + (int64_t)s * kD);
+            v1[k] = *reinterpret_cast<const f32x4 *>(a.ws + ob + (int64_t)s * kD + 4);
         }
         float Mn = M;
 #pragma unroll
@@ -1227,14 +1258,15 @@ static int head_tiles(int H, int layout) { return H > 16 && layout == 0 ? 2 : 1;
 
 constexpr int kMaxSplits = 32;     // K <= 65536 with 2048 entries per split
 
-// Splits per (token, head block): enough workgroups to cover the CUs for
-// small batches, and never more than kMaxSplit entries per workgroup.
-int attn_decode_splits(int T, int H, int K, int layout) {
+// Splits per (token, head block): enough workgroups to give each of the
+// device's `cus` compute units one (a workgroup fills a CU), and never more
+// than kMaxSplit entries per workgroup.
+int attn_decode_splits(int T, int H, int K, int layout, int cus) {
     const int hbw = 16 * head_tiles(H, layout);
     const int64_t units = (int64_t)T * ((H + hbw - 1) / hbw);
     const int tiles = K / kTile;
     if (units <= 0 || tiles <= 0) return 1;
-    int64_t s = (DSA_DECODE_TARGET_BLOCKS + units - 1) / units;
+    int64_t s = (max(cus, 1) + units - 1) / units;
     const int64_t s_min = (K + kMaxSplit - 1) / kMaxSplit;
     if (s < s_min) s = s_min;
     if (s > tiles) s = tiles;
@@ -1250,14 +1282,14 @@ static int split_len_for(int K, int splits) {
     return ((tiles + splits - 1) / splits) * kTile;
 }
 
-int attn_splits(int T, int H, int K, int phase, int layout) {
-    return phase == 0 ? attn_decode_splits(T, H, K, layout) : prefill_splits(K);
+int attn_splits(int T, int H, int K, int phase, int layout, int cus) {
+    return phase == 0 ? attn_decode_splits(T, H, K, layout, cus) : prefill_splits(K);
 }
 
 // Layout 0 has the fewest head blocks and so the most splits: its size
 // covers every layout.
-size_t attn_workspace_bytes(int T, int H, int K, int phase) {
-    const int s = attn_splits(T, H, K, phase, 0);
+size_t attn_workspace_bytes(int T, int H, int K, int phase, int cus) {
+    const int s = attn_splits(T, H, K, phase, 0, cus);
     if (s <= 1) return 0;
     size_t b = (size_t)T * H * s * (kD + 2) * sizeof(float);
     return (b + 255) & ~(size_t)255;
@@ -1272,17 +1304,17 @@ static void allow_big_lds(int bytes) {
     (void)e;
 }
 
-template <bool OUT_BF16, int CH, bool F16>
+template <bool OUT_BF16, int CH>
 static void launch_combine(const AttnArgs &a, hipStream_t stream) {
     const dim3 cgrid((unsigned)(((int64_t)a.T * a.H + 3) / 4));
-    attn_combine_kernel<OUT_BF16, CH, F16><<<cgrid, dim3(256), 0, stream>>>(a);
+    attn_combine_kernel<OUT_BF16, CH><<<cgrid, dim3(256), 0, stream>>>(a);
 }
 
-template <bool OUT_BF16, bool F16>
+template <bool OUT_BF16>
 static void launch_combine_s(const AttnArgs &a, hipStream_t stream) {
-    if (a.n_splits <= 2) return launch_combine<OUT_BF16, 2, F16>(a, stream);
-    if (a.n_splits <= 4) return launch_combine<OUT_BF16, 4, F16>(a, stream);
-    return launch_combine<OUT_BF16, 8, F16>(a, stream);
+    if (a.n_splits <= 2) return launch_combine<OUT_BF16, 2>(a, stream);
+    if (a.n_splits <= 4) return launch_combine<OUT_BF16, 4>(a, stream);
+    return launch_combine<OUT_BF16, 8>(a, stream);
 }
 
 template <int LAYOUT, bool QFP8, bool OUT_BF16, int NT>
@@ -1295,7 +1327,7 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
         constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, true, NT>;
         allow_big_lds<kern>(bytes);
         kern<<<grid, dim3(kThreads), bytes, stream>>>(a);
-        launch_combine_s<OUT_BF16, LAYOUT == 0>(a, stream);
+        launch_combine_s<OUT_BF16>(a, stream);
     } else {
         constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, false, NT>;
         allow_big_lds<kern>(bytes);

@@ -40,10 +40,11 @@ struct AttnArgs {
     int32_t *err_count;
 };
 
-// Number of top-k splits for this shape and phase (1 = none).
-int attn_decode_splits(int T, int H, int K, int layout);
-int attn_splits(int T, int H, int K, int phase, int layout);
-size_t attn_workspace_bytes(int T, int H, int K, int phase);
+// Number of top-k splits for this shape and phase (1 = none) on a device
+// with `cus` compute units.
+int attn_decode_splits(int T, int H, int K, int layout, int cus);
+int attn_splits(int T, int H, int K, int phase, int layout, int cus);
+size_t attn_workspace_bytes(int T, int H, int K, int phase, int cus);
 
 hipError_t launch_attn(const AttnArgs &a, int layout, bool q_fp8, bool out_bf16,
                        hipStream_t stream);

@@ -1,10 +1,14 @@
 """Full-size parity: the named workloads at their real sizes, through the same
 entry points and launch configuration the benchmark times.  The device pool is
-poisoned, every used page gets random finite codes, and the pages of a few
-sampled sequences get oracle-written rows (also kept in a host pool that is
-only materialised on those pages).  The writer step runs first; its bytes are
-compared bit for bit.  Sampled tokens are compared with the oracle; every
-token is checked for finiteness, and all-masked tokens for exact zeros."""
+poisoned, every used page gets random finite codes, and the pages of the
+compared tokens' sequences get oracle-written rows (also kept in a host pool
+that is only materialised on those pages).  The writer step runs first; its
+bytes are compared bit for bit.  The tiny decode and the decode batch (the
+headline) are compared with the oracle token by token in full; the larger
+configurations on at least 32 tokens that cover every token residue mod 8
+(the XCD a token's workgroups run on), every head block and every split of
+the top-k list.  Every token is checked for finiteness, and all-masked
+tokens for exact zeros."""
 import numpy as np
 import pytest
 import torch
@@ -117,9 +121,42 @@ def _decode_case(orc, wl, sample):
         _check(orc, wl, host, out, lse, sample, od=od)
 
 
+def _spread_sample(T, n=32, extra=()):
+    """n tokens of [0, T) spread over the batch, n / 8 of each residue mod 8
+    (the XCD all of a token's workgroups run on), plus `extra`."""
+    per = n // 8
+    picks = set(extra)
+    for r in range(8):
+        cand = np.arange(r, T, 8)
+        picks.update(int(x) for x in cand[np.linspace(0, len(cand) - 1, per).round().astype(int)])
+    return sorted(picks)
+
+
+def test_tiny_decode_full(orc):
+    """The tiny decode configuration end to end: the writer fills the
+    sequence's four pages of a poisoned 8-page pool, then every token and
+    head is compared with the oracle (fp32 and bf16 output)."""
+    wl = W.tiny_decode()
+    print(f"full-size case {wl.name}: T={wl.T} H={wl.H} K={wl.K}", flush=True)
+    slots = wl.page_slots(wl.used_pages())
+    lat, _ = W.pool_content(wl.seed, len(slots), W.RAW)
+    host = np.full((wl.num_slots, 512), W.POISON, np.uint8)
+    assert orc.kv_write(lat, slots, host, W.RAW) == 0
+    pool = torch.full((wl.num_slots, 512), W.POISON, dtype=torch.uint8, device=G.DEV)
+    assert G.run_kv_write(lat, slots, pool, W.RAW) == 0
+    assert np.array_equal(G.host(pool), host), "writer bytes differ"
+    di = G.DevInputs(wl)
+    for od in (dsa.DSA_FP32, dsa.DSA_BF16):
+        out, lse, err = G.run_attn(di, pool, phase=0, out_dtype=od)
+        assert err == 0
+        _check(orc, wl, host, out, lse, list(range(wl.T)), od=od)
+
+
 def test_decode_batch_full(orc):
+    """The headline configuration, every one of its 64 tokens (all 16 heads,
+    all four splits of each top-k list) against the oracle."""
     wl = W.decode_batch()
-    _decode_case(orc, wl, [0, 9, 31, 40, 63])
+    _decode_case(orc, wl, list(range(wl.T)))
 
 
 def test_bf16_decode_full(orc):
@@ -137,14 +174,19 @@ def test_rope_decode_full(orc):
 def test_scaled_decode_full(orc):
     wl = W.scaled_decode()
     empty = int(np.nonzero(np.all(wl.topk < 0, axis=1))[0][0])
-    _decode_case(orc, wl, sorted({0, 17, 77, 127, empty}))
+    _decode_case(orc, wl, _spread_sample(wl.T, 32, extra=(empty,)))
 
 
 def test_mixed_decode_full(orc):
+    """Both 32-head blocks of every compared token, over all three top-k
+    widths."""
     wl = W.mixed_decode()
     # the longest sequences put byte offsets of their pages beyond 4 GiB
     far = int(np.argmax(wl.page_table.max(axis=1)))
-    _decode_case(orc, wl, sorted({3, 100, 255, far}))
+    sample = _spread_sample(wl.T, 32, extra=(far,))
+    widths = {int(np.sum(wl.topk[t] >= 0)) for t in sample}
+    assert widths == {1024, 1536, 2048}
+    _decode_case(orc, wl, sample)
 
 
 def test_q8_prefill_full(orc):
@@ -170,5 +212,6 @@ def test_q8_prefill_full(orc):
     out, lse, err = G.run_attn(di, pool, phase=1, q=q8_d, q_scale=sc_d)
     assert err == 0
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
-    _check(orc, wl, host, out, lse, [0, 1, 126, 127, 128, 2047, 4095],
+    _check(orc, wl, host, out, lse,
+           sorted(set(_spread_sample(wl.T, 32)) | {0, 1, 126, 127, 128, 2047, 4095}),
            q8=q8_ref, scale=s_ref)
