@@ -222,6 +222,32 @@ int32_t dsa_sparse_attn_decode(
     float softmax_scale, void *out, int32_t out_dtype, float *lse,
     void *workspace, size_t workspace_bytes, int32_t *err_count, void *stream);
 
+/*
+ * dsa_sparse_attn_decode_noalloc -- dsa_sparse_attn_decode for callers that
+ * cannot allocate device memory (work captured in a graph that must not
+ * allocate, serving loops held to a fixed memory footprint, harnesses that
+ * forbid allocation): the same computation, kernels and arguments, without
+ * the workspace.  The split partials go to a scratch array the library owns
+ * on each GPU it runs on: DSA_DECODE_SCRATCH_BYTES (32 MiB) per GPU,
+ * resident from the first call on that GPU until the process ends.  A call
+ * whose dsa_attn_workspace_bytes(T, H, K, 0) exceeds that returns
+ * DSA_ERR_WORKSPACE before anything is launched (every top-k width up to
+ * 2048 fits on a 256-CU MI355X).  The call allocates nothing.  Every call on
+ * one GPU shares that GPU's scratch, which keeps the last call's contents
+ * (each split overwrites all of its state, so nothing needs clearing): calls
+ * that overlap on one GPU, on different streams, race.  Other arguments and
+ * errors as for dsa_sparse_attn_decode.
+ */
+#define DSA_DECODE_SCRATCH_BYTES (32u << 20)
+int32_t dsa_sparse_attn_decode_noalloc(
+    const void *q, int32_t q_dtype, const float *q_scale, int32_t T, int32_t H,
+    int32_t D, int32_t rope_dim, const void *pool, int64_t num_slots,
+    int32_t layout, int32_t fp8_format, const int32_t *topk, int32_t K,
+    const int32_t *page_table, int32_t page_size, int32_t max_pages,
+    int32_t num_seqs, const int32_t *token_seq, const int32_t *seq_lens,
+    float softmax_scale, void *out, int32_t out_dtype, float *lse,
+    int32_t *err_count, void *stream);
+
 int32_t dsa_sparse_attn_prefill(
     const void *q, int32_t q_dtype, const float *q_scale, int32_t T, int32_t H,
     int32_t D, int32_t rope_dim, const void *pool, int64_t num_slots,

@@ -57,6 +57,8 @@ _ATTN_ARGS = [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32,
               c_int32, c_int32, c_int32, c_void_p, c_void_p, c_float, c_void_p,
               c_int32, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]
 _SIGS["dsa_sparse_attn_decode"] = (c_int32, _ATTN_ARGS)
+# the workspace pointer and its size are the 24th and 25th arguments
+_SIGS["dsa_sparse_attn_decode_noalloc"] = (c_int32, _ATTN_ARGS[:23] + _ATTN_ARGS[25:])
 _SIGS["dsa_sparse_attn_prefill"] = (c_int32, _ATTN_ARGS)
 _SIGS["dsa_topk_transform"] = (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_int32,
                                          c_int32, c_int32, c_void_p, c_void_p, c_int64,
@@ -151,6 +153,22 @@ def dsa_sparse_attn_decode(q, q_dtype, q_scale, T, H, D, rope_dim, pool,
                  page_table, page_size, max_pages, num_seqs, token_seq,
                  seq_lens, softmax_scale, out, out_dtype, lse, workspace,
                  workspace_bytes, err_count, stream)
+
+
+DSA_DECODE_SCRATCH_BYTES = 32 << 20
+
+
+def dsa_sparse_attn_decode_noalloc(q, q_dtype, q_scale, T, H, D, rope_dim, pool,
+                                   num_slots, layout, fp8_format, topk, K,
+                                   page_table, page_size, max_pages, num_seqs,
+                                   token_seq, seq_lens, softmax_scale, out,
+                                   out_dtype, lse=None, err_count=None,
+                                   stream=None) -> int:
+    return _lib.dsa_sparse_attn_decode_noalloc(
+        _p(q), q_dtype, _p(q_scale), T, H, D, rope_dim, _p(pool), num_slots,
+        layout, fp8_format, _p(topk), K, _p(page_table), page_size, max_pages,
+        num_seqs, _p(token_seq), _p(seq_lens), softmax_scale, _p(out), out_dtype,
+        _p(lse), _p(err_count), _s(stream))
 
 
 def dsa_sparse_attn_prefill(q, q_dtype, q_scale, T, H, D, rope_dim, pool,

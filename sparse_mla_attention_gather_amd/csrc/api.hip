@@ -56,6 +56,26 @@ int split_target_cus() {
     return g_cus[dev].load(std::memory_order_relaxed);
 }
 
+// Scratch of the allocation-free decode entry point: the split partials of
+// one call in a device array the library owns (one copy on every GPU the
+// library runs on, resident until the process ends).  Host code never uses
+// the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, and is kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[DSA_DECODE_SCRATCH_BYTES];
+std::atomic<void *> g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device (NULL on failure).
+void *scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 int32_t check_fp8_format(int32_t f) {
     return f == DSA_FP8_E4M3FN ? DSA_OK : DSA_ERR_DTYPE;
 }
@@ -301,6 +321,35 @@ int32_t dsa_sparse_attn_decode(
                     layout, fp8_format, topk, K, page_table, page_size,
                     max_pages, num_seqs, token_seq, seq_lens, softmax_scale,
                     out, out_dtype, lse, workspace, workspace_bytes, err_count,
+                    stream);
+}
+
+int32_t dsa_sparse_attn_decode_noalloc(
+    const void *q, int32_t q_dtype, const float *q_scale, int32_t T, int32_t H,
+    int32_t D, int32_t rope_dim, const void *pool, int64_t num_slots,
+    int32_t layout, int32_t fp8_format, const int32_t *topk, int32_t K,
+    const int32_t *page_table, int32_t page_size, int32_t max_pages,
+    int32_t num_seqs, const int32_t *token_seq, const int32_t *seq_lens,
+    float softmax_scale, void *out, int32_t out_dtype, float *lse,
+    int32_t *err_count, void *stream) {
+    // every argument check first, against a stand-in for the scratch (an
+    // aligned address that is never dereferenced), then the scratch's own
+    // size limit
+    void *const stand_in = reinterpret_cast<void *>(uintptr_t(256));
+    int32_t st = validate_attn(q, q_dtype, q_scale, T, H, D, rope_dim, pool, num_slots,
+                               layout, fp8_format, topk, K, page_table, page_size,
+                               max_pages, num_seqs, token_seq, seq_lens, out, out_dtype,
+                               stand_in, DSA_DECODE_SCRATCH_BYTES, 0);
+    if (st != DSA_OK || T == 0) return st;
+    if (dsa::attn_workspace_bytes(T, H, K, 0, split_target_cus()) > DSA_DECODE_SCRATCH_BYTES)
+        return DSA_ERR_WORKSPACE;
+    if ((st = check_device())) return st;
+    void *ws = scratch_ptr();
+    if (!ws) return DSA_ERR_DEVICE;
+    return run_attn(0, q, q_dtype, q_scale, T, H, D, rope_dim, pool, num_slots,
+                    layout, fp8_format, topk, K, page_table, page_size,
+                    max_pages, num_seqs, token_seq, seq_lens, softmax_scale,
+                    out, out_dtype, lse, ws, DSA_DECODE_SCRATCH_BYTES, err_count,
                     stream);
 }
 

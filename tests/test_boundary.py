@@ -317,3 +317,37 @@ def test_bf16_layout_passes_validation():
         assert st in (dsa.DSA_ERR_DEVICE, dsa.DSA_OK), dsa.dsa_status_string(st)
     st = dsa.dsa_kv_write(**kv_args(layout=dsa.DSA_KV_BF16_1024))
     assert st in (dsa.DSA_ERR_DEVICE, dsa.DSA_OK), dsa.dsa_status_string(st)
+
+
+# ------------------------------------------------ allocation-free decode
+
+def noalloc(**over):
+    a = attn_args(**over)
+    a.pop("workspace")
+    a.pop("workspace_bytes")
+    return dsa.dsa_sparse_attn_decode_noalloc(**a)
+
+
+def test_noalloc_limit_and_rejections():
+    """The allocation-free decode checks its arguments like the decode and
+    refuses, before any launch, a call whose split partials exceed its
+    32 MiB scratch (here 64 tokens x 16 heads x 32 splits of a 65536-wide
+    top-k list: 67 MB)."""
+    assert dsa.DSA_DECODE_SCRATCH_BYTES == 32 << 20
+    need = dsa.dsa_attn_workspace_bytes(64, 16, 65536, 0)
+    assert need > dsa.DSA_DECODE_SCRATCH_BYTES
+    assert noalloc(T=64, H=16, K=65536, num_seqs=64) == dsa.DSA_ERR_WORKSPACE
+    # every top-k width up to 2048 fits, at any batch, on 256 CUs
+    for T, H in [(1, 16), (255, 16), (255, 32), (63, 128), (127, 32)]:
+        assert dsa.dsa_attn_workspace_bytes(T, H, 2048, 0) <= dsa.DSA_DECODE_SCRATCH_BYTES
+    assert noalloc(D=511) == dsa.DSA_ERR_WIDTH_MISMATCH
+    assert noalloc(K=100) == dsa.DSA_ERR_SHAPE
+    assert noalloc(out=FAKE + 2) == dsa.DSA_ERR_ALIGN
+    assert noalloc(T=0, q=None, pool=None, topk=None, out=None) == dsa.DSA_OK
+
+
+def test_noalloc_without_gpu_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert noalloc(K=2048) == dsa.DSA_ERR_DEVICE
