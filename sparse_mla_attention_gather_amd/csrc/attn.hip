@@ -393,32 +393,61 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // 656-byte rows: query rows of 512 + 64, and bqr = the RoPE part of head
     // c, dims dp*32 + g*8 .. +8 (B operand of one bf16 MFMA step per part).
     constexpr int kQRow = kD + (LAYOUT == 2 ? kRopeDim : 0);
+    constexpr int kQRowBytes = kQRow * (QFP8 ? 1 : 2);
+    constexpr int kQChunks = kQRowBytes / 16;        // 16-byte chunks per head row
     bf16x8 bq[QFP8 ? 1 : kQT][QFP8 ? 1 : kSteps];
     i32x8 bq8[QFP8 ? kQT : 1][QFP8 ? kSteps8 : 1];
     bf16x8 bqr;
     float sscale = a.softmax_scale * kLog2e;
     if constexpr (QFP8) sscale *= *a.q_scale;
-    if (!is_v) {
+    // The query registers from `at(hl, byte)`: the address of byte `byte` of
+    // the row of head hb*kHB + hl, in global memory or in the LDS copy.
+    auto load_q = [&](auto at) {
 #pragma unroll
         for (int nt = 0; nt < kQT; nt++) {
-            const int h = hb * kHB + (kRowPair ? ht : nt) * 16 + c;
-            const int64_t qrow = ((int64_t)t * a.H + (h < a.H ? h : 0)) * kQRow;
+            const int hl = (kRowPair ? ht : nt) * 16 + c;
             if constexpr (LAYOUT == 2)
-                bqr = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
-                    reinterpret_cast<const __bf16 *>(a.q) + qrow + kD + dp * 32 + g * 8));
+                bqr = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(at(hl, (kD + dp * 32 + g * 8) * 2)));
             if constexpr (QFP8) {
-                const uint8_t *qp = reinterpret_cast<const uint8_t *>(a.q) + qrow + dp * kDP + g * 32;
 #pragma unroll
-                for (int k2 = 0; k2 < kSteps8; k2++)
-                    bq8[nt][k2] = *reinterpret_cast<const i32x8 *>(qp + k2 * 128);
+                for (int k2 = 0; k2 < kSteps8; k2++) {
+                    const int b = dp * kDP + k2 * 128 + g * 32;
+                    const u32x4 lo = *reinterpret_cast<const u32x4 *>(at(hl, b));
+                    const u32x4 hi = *reinterpret_cast<const u32x4 *>(at(hl, b + 16));
+                    bq8[nt][k2] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                }
             } else {
-                const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + qrow;
 #pragma unroll
                 for (int kk = 0; kk < kSteps; kk++)
                     bq[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
-                        qp + (dp * kChunks + (kk >> 1) * 4 + g) * 16 + (kk & 1) * 8));
+                        at(hl, ((dp * kChunks + (kk >> 1) * 4 + g) * 16 + (kk & 1) * 8) * 2)));
             }
         }
+    };
+    auto q_global = [&](int hl, int byte) {
+        const int h = hb * kHB + hl;
+        return reinterpret_cast<const uint8_t *>(a.q) +
+               ((int64_t)t * a.H + (h < a.H ? h : 0)) * kQRowBytes + byte;
+    };
+    // With a tile buffer that the pipeline fills only after the first tile
+    // has landed (kStageQ), the query goes to LDS by DMA right behind the
+    // prologue, ahead of the first tiles (so the wait for tile 0 covers it),
+    // instead of into registers at the start: loaded at the start, its
+    // latency would be part of the prologue's (every load waited for there
+    // is older).  In the LDS copy, chunk k < 64 of head hl's row sits at
+    // position k ^ (hl & 7), so that the 16 heads' reads spread over the
+    // banks.
+    constexpr bool kStageQ = kNB > kFill0;
+    uint8_t *const qst = lds + (kNB - 1) * L::kBufBytes;
+    static_assert(!kStageQ || kHB * kQRowBytes <= L::kBufBytes, "query copy fits a tile buffer");
+    static_assert((kHB * kQChunks) % 64 == 0, "whole waves of query chunks");
+    auto q_lds = [&](int hl, int byte) {
+        const int k = byte >> 4;
+        return qst + hl * kQRowBytes + ((k < 64 ? k ^ (hl & 7) : k) << 4) + (byte & 15);
+    };
+    if constexpr (!kStageQ) {
+        if (!is_v) load_q(q_global);
     }
 
     // ---- prologue: resolve this split's indices into LDS.  Every load is
@@ -504,18 +533,33 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         n_tiles = __builtin_amdgcn_readfirstlane(max(1, (last + kTile) / kTile));
     }
 
+    // ---- the query copy (kStageQ): chunk i of the block's kHB rows goes to
+    // LDS position i, holding the row's chunk (i % kQChunks) unswizzled
+    if constexpr (kStageQ) {
+        const uint32_t qbase = lds_addr(qst);
+#pragma unroll
+        for (int i0 = 0; i0 < kHB * kQChunks; i0 += kThreads) {
+            if (i0 + w * 64 < kHB * kQChunks) {
+                const int i = i0 + w * 64 + lane;
+                const int hl = i / kQChunks, kp = i % kQChunks;
+                dma16(q_global(hl, (kp < 64 ? kp ^ (hl & 7) : kp) << 4), qbase + (i0 + w * 64) * 16);
+            }
+        }
+    }
     // ---- fill the pipeline: the first kFill0 tiles now, the other buffers
     // once tile 0 has landed (requested all at once, every workgroup's first
-    // tile would come back only with the rest of the burst)
+    // tile would come back only with the rest of the burst); the buffer
+    // holding the query copy once every wave has its query
 #pragma unroll
     for (int i = 0; i < kFill0; i++)
         if (i < n_tiles)
             issue_tile<LAYOUT, NT>(a, lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
                                    i, w, lane);
-    auto fill_rest = [&]() {
+    auto fill_rest = [&](auto last) {
+        constexpr bool LAST = decltype(last)::value;
 #pragma unroll
         for (int i = kFill0; i < kNB; i++)
-            if (i < n_tiles)
+            if (i < n_tiles && (i == kNB - 1) == LAST)
                 issue_tile<LAYOUT, NT>(a, lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
                                        i, w, lane);
     };
@@ -1121,13 +1165,22 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         // (each role keeps its own registers: nothing flows from one role's
         // code into the other's)
         auto first_tile = [&](auto read_ops) {
+            // tile 0 (and the query copy, issued before it) landed
             wait_tile(0, kFill0 - 1);
             barrier_raw();
-            fill_rest();
+            if constexpr (kStageQ) {
+                fill_rest(std::false_type{});
+                if (!is_v) load_q(q_lds);
+            } else {
+                fill_rest(std::false_type{});
+                fill_rest(std::true_type{});
+            }
             read_ops();
             const TileSlots nsl = read_slots<LAYOUT>(slots, min(kNB, n_tiles - 1) * kTile, w, lane);
             wait_lgkm0();
             barrier_raw();
+            // every wave holds its query: its buffer takes its tile
+            if constexpr (kStageQ) fill_rest(std::true_type{});
             if (!kLate && kNB < n_tiles) issue_tile<LAYOUT, NT>(a, lds0, nsl, 0, kNB % kNScale, w, lane);
         };
         // (the role test goes through readfirstlane so that the compiler
