@@ -1060,7 +1060,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         }
     };
     using DT0 = std::integral_constant<int, 0>;
-    using DTH = std::integral_constant<int, kDT / 2>;
+    using DTH = std::integral_constant<int, 1>;
     using DTN = std::integral_constant<int, kDT>;
     auto pv = [&](int j, auto tpar) {
         pv_prep(j);
@@ -1144,11 +1144,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     using I1 = std::integral_constant<int, 1>;
     {
         // Tile k (parity PAR = k & 1), its operands already in registers:
-        //   scoring waves: QK(k) -> partials; PV waves: the first half of
-        //   tile k-1's dims (P buffer PAR^1, tv[PAR^1]);  [tile k+1 landed]
-        //   barrier;  scoring waves read tile k+1's row chunks, owners turn
-        //   tile k's scores into P (buffer PAR); PV waves: the other half,
-        //   then read tile k+1's transpose operands into tv[PAR^1];  barrier;
+        //   scoring waves: QK(k) -> partials; PV waves: P of tile k-1 (P
+        //   buffer PAR^1) and the first of their four dim tiles (tv[PAR^1]);
+        //   [tile k+1 landed]  barrier;  scoring waves read tile k+1's row
+        //   chunks, owners turn tile k's scores into P (buffer PAR); PV
+        //   waves: the other three dim tiles (after the barrier, where they
+        //   overlap the softmax rather than hold up the scoring waves; one
+        //   or none before it measured alike, two or three slower), then read tile
+        //   k+1's transpose operands into tv[PAR^1];  barrier;
         //   tile k+1's buffer takes tile k+1+kNBuf.
         // Both roles pass the same barriers in the same order.
         // 32 heads (kLate): the PV waves read tile k's transpose operands in
@@ -1228,9 +1231,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 qk(k);
                 wait_tile(k + 1, k + kAhead);
                 barrier_raw();
-                const bool pre = !kOwnStep && k + 1 < n_tiles;
-                if (owner) softmax(k, [&] { if (pre) read_xc(k + 1); });
-                else if (pre) read_xc(k + 1);
+                // (the next tile's chunks are read on every step: past the
+                // last tile the read takes a stale buffer and is not used)
+                if (kRowPair || NT == 2 || dp == 0) softmax(k, [&] { if constexpr (!kOwnStep) read_xc(k + 1); });
+                else if constexpr (!kOwnStep) read_xc(k + 1);
                 wait_lgkm0();
                 barrier_raw();
                 refill(k, nsl);
