@@ -15,7 +15,8 @@
 //
 //   prologue: the split's indices are resolved once (top-k value -> page
 //     table -> slot; -1 for padding and for invalid values, which are also
-//     counted) into LDS; the token's page-table row is staged in LDS next to
+//     counted) into LDS, as each entry's 64-bit row address (a zero row for
+//     a masked entry); the token's page-table row is staged in LDS next to
 //     the top-k loads when it fits;
 //   gather:   rows move HBM -> LDS with global_load_lds_dwordx4 (16 bytes per
 //     lane, no registers) in 64-row tiles through 4 LDS buffers.  Every wave
@@ -108,9 +109,10 @@ struct Lds {
     static constexpr int kScBytes = kTile * 16;                  // 1 KB scales
     static constexpr int kRopeTile = kTile * 2 * kRopeDim;       // 8 KB RoPE parts
     static constexpr int kOffScales = kNB * kBufBytes;
+    // the entries' row sources (64-bit addresses, see kMaskedBit)
     static constexpr int kOffSlots = kOffScales + (kHasScales ? kNScale * kScBytes : 0);
     // partial S^T of the waves holding dim parts 1.. (16 x 16 fp32 each)
-    static constexpr int kOffSp = kOffSlots + kMaxSplit * 4;
+    static constexpr int kOffSp = kOffSlots + kMaxSplit * 8;
     static constexpr int kSpBytes = NT * (kParts - 1) * 4 * 1024;
     // P ([kHB][64] 16-bit, swizzled; the lo terms follow the hi terms): one
     // buffer, since the PV waves hold tile k's P in registers before the
@@ -234,16 +236,28 @@ __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_base) {
 }
 #pragma clang diagnostic pop
 
-// Slots of the rows this wave copies for one tile (see issue_tile).
+// Bytes of one pool row of a layout.
+template <int LAYOUT>
+constexpr int64_t row_bytes() {
+    return LAYOUT == 0 ? kRawBytes : LAYOUT == 1 ? kScaledBytes : LAYOUT == 2 ? kRopeRowBytes : kBf16RowBytes;
+}
+
+// An entry's row source, resolved once in the prologue: the row's address in
+// the pool, or for a masked entry the address of zero row (entry mod 64) of
+// kZeroRow with bit 63 set (the mark of a masked entry; cleared before use).
+// The tile DMA then forms each lane's address with two instructions.
+constexpr uint64_t kMaskedBit = 1ull << 63;
+
+// Row sources of the rows this wave copies for one tile (see issue_tile).
 struct TileSlots {
-    int32_t row[kLoadsRaw];
-    int32_t sc;     // the scale words' row (lanes 0-3)
-    int32_t rp;     // the RoPE part's row (lanes 0-31)
-    int32_t r4[kRowsPerWave];   // bf16 rows: the wave's rows, one per instruction
+    uint64_t row[kLoadsRaw];
+    uint64_t sc;     // the scale words' row (lanes 0-3)
+    uint64_t rp;     // the RoPE part's row (lanes 0-31)
+    uint64_t r4[kRowsPerWave];   // bf16 rows: the wave's rows, one per instruction
 };
 
 template <int LAYOUT>
-__device__ __forceinline__ TileSlots read_slots(const int32_t *slots, int tile_base, int w, int lane) {
+__device__ __forceinline__ TileSlots read_slots(const uint64_t *slots, int tile_base, int w, int lane) {
     TileSlots s;
     const int r0 = kRowsPerWave * w;
 #pragma unroll
@@ -263,19 +277,14 @@ __device__ __forceinline__ TileSlots read_slots(const int32_t *slots, int tile_b
 // parts (lane l -> row 4w + (l >> 3), position l & 7 of the row's 128 bytes
 // in ring slot `buf`, holding chunk (l & 7) ^ swz(row)).
 template <int LAYOUT, int NT>
-__device__ __forceinline__ void issue_tile(const AttnArgs &a, uint32_t lds0, const TileSlots &s,
+__device__ __forceinline__ void issue_tile(uint32_t lds0, const TileSlots &s,
                                            int buf, int sbuf, int w, int lane) {
     using L = Lds<NT, LAYOUT>;
-    constexpr int64_t kRow = LAYOUT == 0 ? kRawBytes : LAYOUT == 1 ? kScaledBytes
-                             : LAYOUT == 2 ? kRopeRowBytes : kBf16RowBytes;
     const int r0 = kRowsPerWave * w;
     const uint32_t dst = lds0 + buf * L::kBufBytes + r0 * L::kRowPitch;
-    // A masked entry (slot < 0) reads zero row r of kZeroRow instead.  The
-    // source is one selected base plus one offset, so that the compiler has
-    // no per-lane 64-bit zero-row address to keep live across the tile loop.
-    auto src_of = [&](int32_t slot, int r, int byte) {
-        const uint8_t *base = slot >= 0 ? a.pool : kZeroRow;
-        return base + (int64_t)(slot >= 0 ? slot : r) * kRow + byte;
+    // (a masked entry's source is its zero row of kZeroRow)
+    auto src_of = [](uint64_t src, int byte) {
+        return reinterpret_cast<const uint8_t *>((src & ~kMaskedBit) + (uint64_t)byte);
     };
     if constexpr (LAYOUT == 3) {
         // one 1024-byte row per instruction: lane l -> position l, holding
@@ -283,7 +292,7 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, uint32_t lds0, con
 #pragma unroll
         for (int k = 0; k < kRowsPerWave; k++) {
             const int r = r0 + k;
-            dma16(src_of(s.r4[k], r, (lane ^ swz(r)) * 16), dst + k * 1024);
+            dma16(src_of(s.r4[k], (lane ^ swz(r)) * 16), dst + k * 1024);
         }
         return;
     }
@@ -291,16 +300,16 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, uint32_t lds0, con
 #pragma unroll
     for (int k = 0; k < kLoadsRaw; k++) {
         const int r = r0 + 2 * k + (lane >> 5);
-        dma16(src_of(s.row[k], r, (pos ^ swz(r)) * 16), dst + k * 1024);
+        dma16(src_of(s.row[k], (pos ^ swz(r)) * 16), dst + k * 1024);
     }
     if (LAYOUT == 1 || LAYOUT == 2) {
         if (lane < kRowsPerWave)
-            dma16(src_of(s.sc, r0 + lane, kD), lds0 + L::kOffScales + sbuf * L::kScBytes + r0 * 16);
+            dma16(src_of(s.sc, kD), lds0 + L::kOffScales + sbuf * L::kScBytes + r0 * 16);
     }
     if (LAYOUT == 2) {
         if (lane < 8 * kRowsPerWave) {
             const int r = r0 + (lane >> 3);
-            dma16(src_of(s.rp, r, kScaledBytes + ((lane & 7) ^ swz(r)) * 16),
+            dma16(src_of(s.rp, kScaledBytes + ((lane & 7) ^ swz(r)) * 16),
                   lds0 + L::kOffRope + buf * L::kRopeTile + r0 * 2 * kRopeDim);
         }
     }
@@ -361,7 +370,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int dp = kRowPair ? (w >> 1) & 1 : (w >> 2) % kParts;      // QK: dims part
     const int wq = kRowPair ? 2 * rh + dp : w & 3;   // entry quarter owned (and scored)
     const int ht = kRowPair ? (w >> 2) & 1 : (NT == 1 ? 0 : dp);
-    const bool owner = !is_v && (kRowPair || NT == 2 || dp == 0);
+    // (owns: the ownership of a scoring wave, a constant with 32 heads)
+    const bool owns = kRowPair || NT == 2 || dp == 0;
+    const bool owner = !is_v && owns;
     const int dbase = 64 * (w - 8);              // PV: first of this wave's dims
     const int n_hb = (a.H + kHB - 1) / kHB;
 
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int hb = (kq % per_tok) / a.n_splits;
     const int split = kq % a.n_splits;
 
-    int32_t *slots = reinterpret_cast<int32_t *>(lds + L::kOffSlots);
+    uint64_t *slots = reinterpret_cast<uint64_t *>(lds + L::kOffSlots);   // row sources
     float *sp_lds = reinterpret_cast<float *>(lds + L::kOffSp);     // [waves][16 heads][16]
     float *rl_lds = reinterpret_cast<float *>(lds + L::kOffRedL);   // [kHB][4 quarters]
 
@@ -508,7 +519,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             bool err;
             const int32_t s = resolve_entry(a, v[i], phys[i], seq_ok, seq_len, err);
             n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(err));   // the wave's
-            if (j < n_ent) slots[j] = s;
+            if (j < n_ent)
+                slots[j] = s >= 0 ? reinterpret_cast<uint64_t>(a.pool + (int64_t)s * row_bytes<LAYOUT>())
+                                  : reinterpret_cast<uint64_t>(kZeroRow + (j & (kTile - 1)) * row_bytes<LAYOUT>()) | kMaskedBit;
             const uint64_t vb = __builtin_amdgcn_ballot_w64(j < n_ent && s >= 0);
             if (vb) last = max(last, w * 64 + 63 - (int)__builtin_clzll(vb) + i * kThreads);
         }
@@ -553,14 +566,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < kFill0; i++)
         if (i < n_tiles)
-            issue_tile<LAYOUT, NT>(a, lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
+            issue_tile<LAYOUT, NT>(lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
                                    i, w, lane);
     auto fill_rest = [&](auto last) {
         constexpr bool LAST = decltype(last)::value;
 #pragma unroll
         for (int i = kFill0; i < kNB; i++)
             if (i < n_tiles && (i == kNB - 1) == LAST)
-                issue_tile<LAYOUT, NT>(a, lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
+                issue_tile<LAYOUT, NT>(lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
                                        i, w, lane);
     };
 
@@ -706,9 +719,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 }
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    float s = 0.0f;
+                    float s = !kScaled ? accg[0][i] : accg[0][i] * scv[i][0];
 #pragma unroll
-                    for (int k2 = 0; k2 < kSteps8; k2++)
+                    for (int k2 = 1; k2 < kSteps8; k2++)
                         s += !kScaled ? accg[k2][i] : accg[k2][i] * scv[i][k2];
                     part[nt][i] = s;
                 }
@@ -793,7 +806,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         float *mq_w = reinterpret_cast<float *>(lds + L::kOffMq + par * L::kMqBytes);
         uint8_t *p_w = lds + L::kOffP;
         const int hh = ht * 16 + c;
-        const int4 sl4 = *reinterpret_cast<const int4 *>(slots + j * kTile + 16 * wq + 4 * g);
+        // (the high words of the entries' row sources: negative when masked)
+        const int32_t *slh = reinterpret_cast<const int32_t *>(slots + j * kTile + 16 * wq + 4 * g) + 1;
+        const int4 sl4 = {slh[0], slh[2], slh[4], slh[6]};
         // own part of the owned (quarter, head tile) plus the other part's,
         // published
         f32x4 s;
@@ -1162,7 +1177,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         auto refill = [&](int k, const TileSlots &nsl) {
             const int nx = k + 1 + kAhead;
             if (nx < n_tiles)
-                issue_tile<LAYOUT, NT>(a, lds0, nsl, nx % kNB, nx % kNScale, w, lane);
+                issue_tile<LAYOUT, NT>(lds0, nsl, nx % kNB, nx % kNScale, w, lane);
         };
         // tile 0's operands, then (16 heads) its buffer takes tile kNBuf
         // (each role keeps its own registers: nothing flows from one role's
@@ -1184,7 +1199,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             barrier_raw();
             // every wave holds its query: its buffer takes its tile
             if constexpr (kStageQ) fill_rest(std::true_type{});
-            if (!kLate && kNB < n_tiles) issue_tile<LAYOUT, NT>(a, lds0, nsl, 0, kNB % kNScale, w, lane);
+            if (!kLate && kNB < n_tiles) issue_tile<LAYOUT, NT>(lds0, nsl, 0, kNB % kNScale, w, lane);
         };
         // (the role test goes through readfirstlane so that the compiler
         // sees a uniform branch and gives each role its own registers)
@@ -1231,9 +1246,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 qk(k);
                 wait_tile(k + 1, k + kAhead);
                 barrier_raw();
-                // (the next tile's chunks are read on every step: past the
-                // last tile the read takes a stale buffer and is not used)
-                if (kRowPair || NT == 2 || dp == 0) softmax(k, [&] { if constexpr (!kOwnStep) read_xc(k + 1); });
+                // The next tile's chunks are read on every step (past the
+                // last tile from a stale buffer, unused), and an owner is
+                // told apart by `owns` rather than `owner`, whose role test
+                // the compiler does not see as settled here: each way, the
+                // chunks have a single definition per step and keep their
+                // registers across the loop instead of being copied.
+                if (owns) softmax(k, [&] { if constexpr (!kOwnStep) read_xc(k + 1); });
                 else if constexpr (!kOwnStep) read_xc(k + 1);
                 wait_lgkm0();
                 barrier_raw();
