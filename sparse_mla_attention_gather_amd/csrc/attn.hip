@@ -22,7 +22,7 @@
 //     lane, no registers) in 64-row tiles through 4 LDS buffers.  Every wave
 //     copies the operands it needs from a landed tile into registers at once,
 //     so a buffer is refilled as soon as all waves hold their copy.  The
-//     16-byte chunks of row r are stored XOR-swizzled by (r & 7) so that the
+//     16-byte chunks of row r are stored XOR-swizzled by (r & 15) so that the
 //     matrix-operand reads spread over the LDS banks; masked entries read
 //     zero rows;
 //   QK^T:     wave w forms a 16 x 16 partial S^T: entries 16(w%4) .. +16, one
@@ -207,16 +207,27 @@ __device__ __forceinline__ int32_t resolve_entry(const AttnArgs &a, int32_t i,
                          a.max_pages, a.num_slots, err);
 }
 
-__device__ __forceinline__ int swz(int row) { return row & 7; }
+// LDS bank spreading.  A 16-byte-per-lane access serves 16 lanes at a time
+// over the 64 four-byte banks (256 bytes), so the 16 rows c = 0..15 that
+// such an access touches must land on 16 distinct 16-byte positions of a
+// 256-byte period: the chunks of a row (512-byte pitch) are XOR-swizzled by
+// row & 15 (measured against row & 7: half the bank-conflict cycles, Q8
+// prefill -2.5 %).  1024-byte bf16 rows keep row & 7 (their 2-byte PV reads
+// would otherwise not fit the registers), and so does the 8-chunk ring of
+// RoPE parts.
+template <int LAYOUT>
+__device__ __forceinline__ int swz(int row) { return LAYOUT == 3 ? row & 7 : row & 15; }
+__device__ __forceinline__ int swz8(int row) { return row & 7; }
 
-// The partial-score rows ([head][4 entry groups of 4]) rotate their groups by
-// (c & 7) >> 1 so that eight consecutive lanes c of a 16-byte access fall on
+// The partial-score rows ([head][4 entry groups of 4], 64 bytes) rotate
+// their groups by c >> 2, so that the 16 lanes c of a 16-byte access fall on
 // distinct banks.
-__device__ __forceinline__ int sp_slot(int grp, int c) { return (grp + ((c & 7) >> 1)) & 3; }
+__device__ __forceinline__ int sp_slot(int grp, int c) { return (grp + (c >> 2)) & 3; }
 
 // Byte offset of the 16-byte P chunk k (entries 8k .. 8k+7) of head row hh:
-// rows of 128 bytes, chunks XOR-swizzled by hh & 7.
-__device__ __forceinline__ int p_off(int hh, int k) { return hh * 128 + ((k ^ (hh & 7)) << 4); }
+// rows of 128 bytes, chunks XOR-swizzled by (hh >> 1) & 7 (rows hh and hh + 2
+// share banks; 16 consecutive rows cover them once).
+__device__ __forceinline__ int p_off(int hh, int k) { return hh * 128 + ((k ^ ((hh >> 1) & 7)) << 4); }
 
 // 32-bit LDS address of a pointer into dynamic shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -272,10 +283,10 @@ __device__ __forceinline__ TileSlots read_slots(const uint64_t *slots, int tile_
 // Issue the DMA of one 64-row tile into data buffer `buf` and scale buffer
 // `sbuf`: wave w moves rows [4w, 4w+4), two rows per instruction (lane l ->
 // row 4w + 2k + (l >> 5), LDS chunk position l & 31, holding global chunk
-// (l & 31) ^ swz(row)); scaled rows add one 4-lane instruction for the rows'
+// (l & 31) ^ swz<LAYOUT>(row)); scaled rows add one 4-lane instruction for the rows'
 // 16-byte scale words; 656-byte rows one 32-lane instruction for their RoPE
 // parts (lane l -> row 4w + (l >> 3), position l & 7 of the row's 128 bytes
-// in ring slot `buf`, holding chunk (l & 7) ^ swz(row)).
+// in ring slot `buf`, holding chunk (l & 7) ^ swz<LAYOUT>(row)).
 template <int LAYOUT, int NT>
 __device__ __forceinline__ void issue_tile(uint32_t lds0, const TileSlots &s,
                                            int buf, int sbuf, int w, int lane) {
@@ -288,11 +299,11 @@ __device__ __forceinline__ void issue_tile(uint32_t lds0, const TileSlots &s,
     };
     if constexpr (LAYOUT == 3) {
         // one 1024-byte row per instruction: lane l -> position l, holding
-        // chunk l ^ swz(row)
+        // chunk l ^ swz<LAYOUT>(row)
 #pragma unroll
         for (int k = 0; k < kRowsPerWave; k++) {
             const int r = r0 + k;
-            dma16(src_of(s.r4[k], (lane ^ swz(r)) * 16), dst + k * 1024);
+            dma16(src_of(s.r4[k], (lane ^ swz<LAYOUT>(r)) * 16), dst + k * 1024);
         }
         return;
     }
@@ -300,7 +311,7 @@ __device__ __forceinline__ void issue_tile(uint32_t lds0, const TileSlots &s,
 #pragma unroll
     for (int k = 0; k < kLoadsRaw; k++) {
         const int r = r0 + 2 * k + (lane >> 5);
-        dma16(src_of(s.row[k], (pos ^ swz(r)) * 16), dst + k * 1024);
+        dma16(src_of(s.row[k], (pos ^ swz<LAYOUT>(r)) * 16), dst + k * 1024);
     }
     if (LAYOUT == 1 || LAYOUT == 2) {
         if (lane < kRowsPerWave)
@@ -309,7 +320,7 @@ __device__ __forceinline__ void issue_tile(uint32_t lds0, const TileSlots &s,
     if (LAYOUT == 2) {
         if (lane < 8 * kRowsPerWave) {
             const int r = r0 + (lane >> 3);
-            dma16(src_of(s.rp, kScaledBytes + ((lane & 7) ^ swz(r)) * 16),
+            dma16(src_of(s.rp, kScaledBytes + ((lane & 7) ^ swz8(r)) * 16),
                   lds0 + L::kOffRope + buf * L::kRopeTile + r0 * 2 * kRopeDim);
         }
     }
@@ -631,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         for (int rt = 0; rt < kRT; rt++) {
             const int r = 16 * (kRowPair ? 2 * rh + rt : wq) + c;
             const uint8_t *xr = lds + (j % kNB) * L::kBufBytes + r * L::kRowPitch;
-            const int sw = swz(r);
+            const int sw = swz<LAYOUT>(r);
 #pragma unroll
             for (int m = 0; m < kXc; m++) {
                 // bf16 rows: step m's 8 dims (the query's d of step m) are the
@@ -644,7 +655,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             if constexpr (LAYOUT == 2) {
                 // RoPE dims dp*32 + g*8 .. +8 of the same row: chunk dp*4 + g
                 const uint8_t *rr = lds + L::kOffRope + (j % kNB) * L::kRopeTile + r * (2 * kRopeDim);
-                xcr = *reinterpret_cast<const u32x4 *>(rr + (((dp * 4 + g) ^ sw) * 16));
+                xcr = *reinterpret_cast<const u32x4 *>(rr + (((dp * 4 + g) ^ swz8(r)) * 16));
             }
         }
     };
@@ -668,7 +679,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                     for (int i = 0; i < 8; i++) {
                         const int e = ks * 32 + g * 8 + i;
                         hw[i] = *reinterpret_cast<const uint16_t *>(
-                            xb + e * 1024 + (((dim >> 3) ^ swz(e)) * 16) + (dim & 7) * 2);
+                            xb + e * 1024 + (((dim >> 3) ^ swz<LAYOUT>(e)) * 16) + (dim & 7) * 2);
                     }
                     tv[PAR][ks][dt] = u32x4{hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16),
                                             hw[4] | (hw[5] << 16), hw[6] | (hw[7] << 16)};
@@ -681,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             for (int ks = 0; ks < 2; ks++) {
                 const int row = ks * 32 + g * 8 + (c >> 1);
                 const uint8_t *rp = xb + row * 512 + (c & 1) * 8;
-                const int sw = swz(row);
+                const int sw = swz<LAYOUT>(row);
 #pragma unroll
                 for (int dt = 0; dt < kDT; dt++)
                     tv[PAR][ks][dt] = __builtin_bit_cast(
