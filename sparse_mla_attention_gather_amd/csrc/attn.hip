@@ -12,6 +12,8 @@
 // list (at most 2048 entries).  All heads of the block share every gathered
 // row, so Q.X^T is a real [16NT x 512] x [512 x entries] contraction for the
 // matrix cores, and a row is gathered once per block of up to 32 heads.
+// (An FP8 query in 32-head blocks runs attn_q8_kernel further down: eight
+// wavefronts of 256 registers, one barrier per tile.)
 //
 //   prologue: the split's indices are resolved once (top-k value -> page
 //     table -> slot; -1 for padding and for invalid values, which are also
@@ -19,38 +21,36 @@
 //     a masked entry); the token's page-table row is staged in LDS next to
 //     the top-k loads when it fits;
 //   gather:   rows move HBM -> LDS with global_load_lds_dwordx4 (16 bytes per
-//     lane, no registers) in 64-row tiles through 4 LDS buffers.  Every wave
-//     copies the operands it needs from a landed tile into registers at once,
-//     so a buffer is refilled as soon as all waves hold their copy.  The
-//     16-byte chunks of row r are stored XOR-swizzled by (r & 15) so that the
-//     matrix-operand reads spread over the LDS banks; masked entries read
-//     zero rows;
-//   QK^T:     wave w forms a 16 x 16 partial S^T: entries 16(w%4) .. +16, one
-//     head tile, one part of the 512 dims (NT = 1: four 128-dim quarters;
-//     NT = 2: two 256-dim halves x two head tiles).  bf16 query:
+//     lane, no registers) in 64-row tiles through up to 4 LDS buffers.
+//     Every wave copies the operands it needs from a landed tile into
+//     registers at once, so a buffer is refilled as soon as all waves hold
+//     their copy.  The 16-byte chunks of row r are stored XOR-swizzled by
+//     (r & 15) so that the matrix-operand reads spread over the LDS banks;
+//     masked entries read zero rows;
+//   QK^T:     waves 0-7 form 16 x 16 partial S^T blocks: 16 entries, one head
+//     tile, one 256-dim half of the dims.  bf16 query:
 //     v_mfma_f32_16x16x32_bf16 on rows converted FP8 -> bf16 exactly (exact
 //     products, fp32 sums); FP8 query: v_mfma_scale_f32_16x16x128_f8f6f4 on
 //     the codes themselves (unit block scales), the query scale folded into
 //     the score scale;
-//   softmax:  the wave holding part 0 of an entry quarter adds the other
-//     parts (through LDS), keeps its own running maximum per head (log2
-//     domain, moved only when exceeded by more than kSlack, so P <= 2^kSlack)
-//     and denominator, and publishes P (f16) and its maximum;
-//   PV:       wave w accumulates O^T for dims [32w, 32w+32) over the 64
-//     entries with v_mfma_f32_16x16x32_f16, against a per-head reference
-//     maximum M that tracks the largest quarter maximum; P of quarter q is
-//     weighted by 2^(m_q - M) <= 1 on the way into the f16 operand.  The A
-//     operand (8 entries x 1 dim per lane) comes from the row-major tile
-//     through the gfx950 LDS transpose read ds_read_b64_tr_b8.  528-byte
-//     rows: group scales multiply the QK partial sums per 128-wide group and,
-//     in PV, multiply P (normalised per tile by the largest scale, the factor
-//     applied to the tile's f32 product);
-//   schedule: with 16 heads, PV runs one tile behind QK and the next tile's
-//     operands are read from LDS while the owners' softmax and the PV run,
-//     so the LDS traffic (each row is read twice, once per layout) overlaps
-//     the latency-bound phases; two barriers per tile;
-//   epilogue: normalised output + lse, or (several splits) unnormalised
-//     partial (o, m, l) states that a second kernel merges.
+//   softmax:  the owner of an (entry quarter, head tile) adds the other
+//     half's partial (through LDS), keeps its own running maximum per head
+//     (log2 domain, moved only when exceeded by more than kSlack, so
+//     P <= 2^kSlack) and publishes P (f16; bf16 for bf16 rows) and its
+//     maximum;
+//   PV:       waves 8-15 accumulate O^T for 64 dims each over the 64 entries
+//     with v_mfma_f32_16x16x32_f16, against a per-head reference maximum
+//     that tracks the largest quarter maximum; P of quarter q is weighted by
+//     2^(m_q - m_ref) <= 1 on the way into the f16 operand.  The A operand
+//     (8 entries x 1 dim per lane) comes from the row-major tile through the
+//     gfx950 LDS transpose read ds_read_b64_tr_b8.  Group-scaled rows scale
+//     the QK partial sums per 128-wide group and multiply P by each entry's
+//     scale over the running largest scale of its group;
+//   schedule: PV runs one tile behind QK, the next tile's operands are read
+//     from LDS while the owners' softmax and the PV run; two barriers per
+//     tile;
+//   epilogue: normalised output + lse, or (several splits) the normalised
+//     fp32 output and (m, l) of each split, which a second kernel merges.
 //
 // All workgroups of one token are numbered b = 8k + (t mod 8), so with the
 // round-robin workgroup-to-XCD dispatch they share one XCD's L2.
@@ -343,6 +343,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // overlaps the PV of tile k-1 and each tile's operand reads overlap the
     // phase before.
     static_assert(kParts == 2, "one publishing wave per head tile and quarter");
+    static_assert(!(QFP8 && NT == 2), "FP8 query in 32-head blocks: attn_q8_kernel");
     // PV operands read in their own step (one register set; a tile's buffer
     // is refilled right after its step): 32-head blocks and 656-byte rows,
     // whose extra operands would not fit otherwise
@@ -364,9 +365,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // partial through LDS slot ht*4 + q):
     //   16 heads: wave (q = w & 3, dp = w >> 2) scores quarter q; the dp = 0
     //     waves own their quarter, the dp = 1 waves only publish;
-    //   32 heads, FP8 query: wave (q, dp) scores quarter q of both head
-    //     tiles (each converted row operand feeds two MFMAs) and owns head
-    //     tile dp;
+    //   32 heads, FP8 query: run by attn_q8_kernel (eight waves), not here;
     //   32 heads, bf16 query (kRowPair: the query of both head tiles would
     //     not fit the 128 registers a lane has at 16 waves per CU): wave
     //     (rh = w & 1, dp = (w >> 1) & 1, ht = w >> 2) scores quarters 2rh
@@ -1273,6 +1272,464 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         }
     }
 }
+// ===========================================================================
+// FP8 query over raw rows in 32-head blocks: eight wavefronts of 256
+// registers (two per SIMD) instead of sixteen of 128.
+//
+// The sixteen-wave kernel above splits a 32-head block's QK^T over two
+// 256-dim halves, whose partial scores cross waves through LDS, and has each
+// of its eight PV waves read all of P: about 150 KB of LDS traffic per
+// 64-entry tile, which sets its pace.  With 256 registers a lane:
+//   waves 0-3 (scoring, entry quarter q = w) hold the query of both head
+//     tiles over all 512 dims and score their quarter completely (eight FP8
+//     MFMAs per tile), then run the softmax of both head tiles.  They also
+//     copy their own quarter's 16 rows of every tile, so that each waits for
+//     its rows with vmcnt alone and reads the next tile's row chunks during
+//     the softmax, with no barrier in between;
+//   waves 4-7 (PV, dims 128 (w - 4) .. +128) accumulate both head tiles one
+//     tile behind: P of tile k-1 and the transpose operands read in step
+//     k-1, then tile k's operands.
+// One barrier per tile: every scoring wave has waited for its rows of tile
+// k+1 before barrier k, so the PV waves read that tile after it; P, the
+// quarter maxima and the flags are double-buffered by tile parity.  LDS
+// traffic per tile: DMA 32 KB, row chunks 32 KB, P 4 + 16 KB, transpose
+// operands 32 KB.  Numerics are those of the sixteen-wave kernel (the same
+// products, the same lazy maximum, one f16 term of P, the denominator from
+// the P operand itself).
+struct W8 {
+    static constexpr int kWaves = 8;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kNB = 4;                              // tile buffers
+    static constexpr int kHB = 32;                             // heads per block
+    static constexpr int kBufBytes = kTile * kRawBytes;        // 32 KB
+    static constexpr int kOffSlots = kNB * kBufBytes;          // row sources (16 KB)
+    static constexpr int kOffP = kOffSlots + kMaxSplit * 8;    // P ([32][64] f16), two
+    static constexpr int kPBytes = kHB * kTile * 2;
+    static constexpr int kOffMq = kOffP + 2 * kPBytes;         // quarter maxima [32][4], two
+    static constexpr int kMqBytes = kHB * 16;
+    static constexpr int kOffRedL = kOffMq + 2 * kMqBytes;     // last entries, then denominators
+    static constexpr int kOffFlags = kOffRedL + kHB * 16;      // [32][4] bytes, two
+    static constexpr int kBytes = kOffFlags + 2 * kHB * 4;
+    static constexpr int kDT = 8;                              // PV: 16-dim tiles per wave
+    static constexpr int kLoads = 8;                           // DMA instructions per scoring wave and tile
+    // the page-table row is staged in tile buffer 2 (free until after the prologue)
+    static constexpr int kPtPer = kBufBytes / 4 / kThreads;
+    static_assert(kBytes <= 160 * 1024, "LDS budget");
+};
+
+template <bool OUT_BF16, bool SPLIT>
+__global__ __launch_bounds__(W8::kThreads) void attn_q8_kernel(AttnArgs a) {
+    using L = W8;
+    constexpr int kNB = L::kNB, kHB = L::kHB, kDT = L::kDT;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 15, g = lane >> 4;
+    const bool is_v = w >= 4;                    // a PV wave
+    const int q = w & 3;                         // scoring: the entry quarter
+    const int dbase = 128 * (w - 4);             // PV: first of this wave's dims
+    const int n_hb = (a.H + kHB - 1) / kHB;
+
+    // XCD-aware numbering, as in attn_kernel
+    const int per_tok = n_hb * a.n_splits;
+    const int x = blockIdx.x & 7;
+    const int kq = blockIdx.x >> 3;
+    const int t = (kq / per_tok) * 8 + x;
+    if (t >= a.T) return;
+    const int hb = (kq % per_tok) / a.n_splits;
+    const int split = kq % a.n_splits;
+
+    uint64_t *slots = reinterpret_cast<uint64_t *>(lds + L::kOffSlots);   // row sources
+    float *rl_lds = reinterpret_cast<float *>(lds + L::kOffRedL);
+    const int seq = a.token_seq ? a.token_seq[t] : t;
+    const bool seq_ok = (a.page_table == nullptr && a.seq_lens == nullptr) ||
+                        (seq >= 0 && seq < a.num_seqs);
+    const int seq_len = (a.seq_lens && seq_ok) ? a.seq_lens[seq] : INT_MAX;
+    const int begin = split * a.split_len;
+    const int n_ent = min(a.K - begin, a.split_len);   // a multiple of 64
+    const float sscale = a.softmax_scale * kLog2e * *a.q_scale;
+
+    // ---- prologue: the split's entries resolved to row sources in LDS (as
+    // in attn_kernel: unconditional loads, the page-table row staged when it
+    // fits, the last valid entry found by ballots)
+    {
+        constexpr int kPer = kMaxSplit / L::kThreads;
+        constexpr int kPtCap = L::kPtPer * L::kThreads;
+        const int32_t *tk = a.topk + (int64_t)t * a.K + begin;
+        const int32_t *row = a.page_table + (int64_t)(seq_ok ? seq : 0) * a.max_pages;
+        int32_t *pt_lds = reinterpret_cast<int32_t *>(lds + 2 * L::kBufBytes);
+        const bool pt_staged = a.page_table != nullptr && a.max_pages <= kPtCap;
+        int32_t v[kPer], phys[kPer];
+        if (pt_staged) {
+            const int npt = (a.max_pages + L::kThreads - 1) / L::kThreads;   // uniform
+            int32_t pw[L::kPtPer];
+#pragma unroll
+            for (int k = 0; k < L::kPtPer; k++)
+                pw[k] = k < npt ? row[min(tid + k * L::kThreads, a.max_pages - 1)] : 0;
+#pragma unroll
+            for (int i = 0; i < kPer; i++) {
+                const int j = tid + i * L::kThreads;
+                const int32_t xv = tk[min(j, n_ent - 1)];
+                v[i] = j < n_ent ? xv : -1;
+            }
+#pragma unroll
+            for (int k = 0; k < L::kPtPer; k++)
+                if (k < npt && tid + k * L::kThreads < a.max_pages) pt_lds[tid + k * L::kThreads] = pw[k];
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kPer; i++)
+                phys[i] = pt_lds[min(max(v[i], 0) >> a.page_shift, a.max_pages - 1)];
+        } else {
+#pragma unroll
+            for (int i = 0; i < kPer; i++) {
+                const int j = tid + i * L::kThreads;
+                const int32_t xv = tk[min(j, n_ent - 1)];
+                v[i] = j < n_ent ? xv : -1;
+            }
+            if (a.page_table) {
+#pragma unroll
+                for (int i = 0; i < kPer; i++)
+                    phys[i] = row[min(max(v[i], 0) >> a.page_shift, a.max_pages - 1)];
+            } else {
+#pragma unroll
+                for (int i = 0; i < kPer; i++) phys[i] = 0;
+            }
+        }
+        int n_err = 0, last = -1;
+#pragma unroll
+        for (int i = 0; i < kPer; i++) {
+            const int j = tid + i * L::kThreads;
+            bool err;
+            const int32_t s = resolve_entry(a, v[i], phys[i], seq_ok, seq_len, err);
+            n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(err));   // the wave's
+            if (j < n_ent)
+                slots[j] = s >= 0 ? reinterpret_cast<uint64_t>(a.pool + (int64_t)s * kRawBytes)
+                                  : reinterpret_cast<uint64_t>(kZeroRow + (j & (kTile - 1)) * kRawBytes) | kMaskedBit;
+            const uint64_t vb = __builtin_amdgcn_ballot_w64(j < n_ent && s >= 0);
+            if (vb) last = max(last, w * 64 + 63 - (int)__builtin_clzll(vb) + i * L::kThreads);
+        }
+        if (lane == 0) reinterpret_cast<int *>(rl_lds)[w] = last;
+        if (a.err_count && hb == 0 && lane == 0 && n_err) atomicAdd(a.err_count, n_err);
+    }
+    __syncthreads();
+    const uint32_t lds0 = lds_addr(lds);
+    int n_tiles;
+    {
+        const int4 *lw = reinterpret_cast<const int4 *>(rl_lds);
+        const int4 v0 = lw[0], v1 = lw[1];
+        const int last = max(max(max(v0.x, v0.y), max(v0.z, v0.w)), max(max(v1.x, v1.y), max(v1.z, v1.w)));
+        n_tiles = __builtin_amdgcn_readfirstlane(max(1, (last + kTile) / kTile));
+    }
+
+    // ---- scoring waves: the tile DMA of their quarter's rows (two rows per
+    // instruction: lane l -> row 16q + 2k + (l >> 5), position l & 31
+    // holding chunk (l & 31) ^ swz(row)), and the wait for their own rows
+    auto row_src = [&](int j, int k) { return slots[j * kTile + 16 * q + 2 * k + (lane >> 5)]; };
+    auto issue = [&](int j, const uint64_t (&src)[L::kLoads]) {
+        const uint32_t dst = lds0 + (j % kNB) * L::kBufBytes + 16 * q * kRawBytes;
+        const int pos = lane & 31;
+#pragma unroll
+        for (int k = 0; k < L::kLoads; k++) {
+            const int r = 16 * q + 2 * k + (lane >> 5);
+            dma16(reinterpret_cast<const uint8_t *>((src[k] & ~kMaskedBit) + (uint64_t)((pos ^ swz<0>(r)) * 16)),
+                  dst + k * 1024);
+        }
+    };
+    auto issue_tile8 = [&](int j) {
+        uint64_t src[L::kLoads];
+#pragma unroll
+        for (int k = 0; k < L::kLoads; k++) src[k] = row_src(j, k);
+        issue(j, src);
+    };
+    // this wave's rows of tile j landed; `issued` is the last tile issued
+    auto wait_own = [&](int j, int issued) {
+        const int ahead = min(issued, n_tiles - 1) - j;
+        if (ahead >= 3) wait_vm_lgkm0<3 * L::kLoads>();
+        else if (ahead == 2) wait_vm_lgkm0<2 * L::kLoads>();
+        else if (ahead == 1) wait_vm_lgkm0<L::kLoads>();
+        else wait_vm_lgkm0<0>();
+    };
+
+    // ---- the query copy (tile buffer 3, chunk k < 64 of head row hl at
+    // position k ^ (hl & 7)), issued by the scoring waves before their first
+    // tiles, so that the wait for tile 0 covers it
+    uint8_t *const qst = lds + 3 * L::kBufBytes;
+    auto q_global = [&](int hl, int byte) {
+        const int h = hb * kHB + hl;
+        return reinterpret_cast<const uint8_t *>(a.q) + ((int64_t)t * a.H + (h < a.H ? h : 0)) * kD + byte;
+    };
+
+    if (__builtin_amdgcn_readfirstlane((int)is_v) == 0) {
+        // ================= scoring waves =================
+        {
+            const uint32_t qbase = lds_addr(qst);
+#pragma unroll
+            for (int i0 = 0; i0 < kHB * 32 / 4; i0 += 64) {
+                const int i = q * (kHB * 32 / 4) + i0 + lane;
+                const int hl = i / 32, kp = i % 32;
+                dma16(q_global(hl, (kp ^ (hl & 7)) << 4), qbase + (q * (kHB * 32 / 4) + i0) * 16);
+            }
+        }
+        issue_tile8(0);
+        if (n_tiles > 1) issue_tile8(1);
+        wait_own(0, 1);
+        barrier_raw();                       // tile 0 and the query copy landed
+        // the query of both head tiles: bq8[nt][k2] = q8[h][128 k2 + 32 g .. +32]
+        i32x8 bq8[2][4];
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+            for (int k2 = 0; k2 < 4; k2++) {
+                const int hl = nt * 16 + c;
+                const int k = 8 * k2 + 2 * g;
+                const u32x4 lo = *reinterpret_cast<const u32x4 *>(qst + hl * kD + ((k ^ (hl & 7)) << 4));
+                const u32x4 hi = *reinterpret_cast<const u32x4 *>(qst + hl * kD + (((k + 1) ^ (hl & 7)) << 4));
+                bq8[nt][k2] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+        // row chunks of the quarter's row 16q + c: K step k2 takes chunks
+        // 8 k2 + 2g and 8 k2 + 2g + 1
+        u32x4 xc[8];
+        auto read_xc = [&](int j) {
+            const int r = 16 * q + c;
+            const uint8_t *xr = lds + (j % kNB) * L::kBufBytes + r * kRawBytes;
+            const int sw = swz<0>(r);
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                const int ch = (m >> 1) * 8 + g * 2 + (m & 1);
+                xc[m] = *reinterpret_cast<const u32x4 *>(xr + ((ch ^ sw) * 16));
+            }
+        };
+        read_xc(0);
+        if (n_tiles > 2) issue_tile8(2);
+        wait_lgkm0();
+        barrier_raw();                       // every scoring wave holds the query
+        if (n_tiles > 3) issue_tile8(3);
+
+        float m_own[2] = {kNoMax, kNoMax};
+        for (int k = 0; k < n_tiles; k++) {
+            // row sources of the tile that refills this step's buffer
+            const int nx = k + kNB;
+            uint64_t nsrc[L::kLoads];
+#pragma unroll
+            for (int i = 0; i < L::kLoads; i++) nsrc[i] = row_src(min(nx, n_tiles - 1), i);
+            // QK^T of both head tiles over the quarter's 16 entries
+            f32x4 part[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++) {
+                f32x4 accg[4];
+#pragma unroll
+                for (int k2 = 0; k2 < 4; k2++) {
+                    const u32x4 &lo = xc[2 * k2], &hi = xc[2 * k2 + 1];
+                    const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    accg[k2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        av, bq8[nt][k2], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; i++) part[nt][i] = (accg[0][i] + accg[1][i]) + (accg[2][i] + accg[3][i]);
+            }
+            // softmax of both head tiles (as attn_kernel's owners): entries
+            // 16q + 4g + i of head nt*16 + c
+            const int par = k & 1;
+            const int32_t *slh = reinterpret_cast<const int32_t *>(slots + k * kTile + 16 * q + 4 * g) + 1;
+            const int32_t slv[4] = {slh[0], slh[2], slh[4], slh[6]};
+            f32x4 mp[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++)
+                mp[nt] = *reinterpret_cast<const f32x4 *>(lds + L::kOffMq + (par ^ 1) * L::kMqBytes + (nt * 16 + c) * 16);
+            // the next tile's row chunks, once this wave's rows of it landed
+            // (past the last tile from a stale buffer, unused)
+            wait_own(k + 1, k + 3);
+            read_xc(k + 1);
+            float *mq_w = reinterpret_cast<float *>(lds + L::kOffMq + par * L::kMqBytes);
+            uint8_t *p_w = lds + L::kOffP + par * L::kPBytes;
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++) {
+                const int hh = nt * 16 + c;
+                float sv[4], mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    sv[i] = slv[i] >= 0 ? part[nt][i] * sscale : -INFINITY;
+                    mx = fmaxf(mx, sv[i]);
+                }
+                mx = max_over_g(mx);
+                if (k > 0) {
+                    const float r = fmaxf(fmaxf(mp[nt][0], mp[nt][1]), fmaxf(mp[nt][2], mp[nt][3]));
+                    m_own[nt] = fmaxf(m_own[nt], r);
+                }
+                const bool moved = mx - m_own[nt] > kSlack;   // false for an all-masked tile
+                if (moved) m_own[nt] = mx;
+                if (g == 0) lds[L::kOffFlags + par * kHB * 4 + hh * 4 + q] = k > 0 && !moved;
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_own[nt]);
+                const f16x2 p01 = {(_Float16)p[0], (_Float16)p[1]};
+                const f16x2 p23 = {(_Float16)p[2], (_Float16)p[3]};
+                *reinterpret_cast<u32x2 *>(p_w + p_off(hh, 2 * q + (g >> 1)) + (g & 1) * 8) =
+                    u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+                if (g == 0) mq_w[hh * 4 + q] = m_own[nt];
+            }
+            wait_lgkm0();
+            barrier_raw();
+            if (nx < n_tiles) issue(nx, nsrc);
+        }
+        __syncthreads();                     // the PV waves' epilogue barrier
+        return;
+    }
+
+    // ================= PV waves =================
+    f32x4 acc[kDT][2], lacc[2];
+    float m_ref[2] = {kNoMax, kNoMax};
+#pragma unroll
+    for (int nt = 0; nt < 2; nt++) {
+        lacc[nt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int dt = 0; dt < kDT; dt++) acc[dt][nt] = f32x4{0, 0, 0, 0};
+    }
+    // transpose operands of a tile: lane (c, g) addresses entry
+    // ks*32 + g*8 + (c >> 1), half (c & 1) of the chunk of dims dbase + 16 dt
+    u32x2 tv[2][kDT];
+    auto read_tv = [&](int j) {
+        const uint8_t *xb = lds + (j % kNB) * L::kBufBytes;
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+            const int row = ks * 32 + g * 8 + (c >> 1);
+            const uint8_t *rp = xb + row * kRawBytes + (c & 1) * 8;
+            const int sw = swz<0>(row);
+#pragma unroll
+            for (int dt = 0; dt < kDT; dt++)
+                tv[ks][dt] = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_i32x2 *>(
+                               LDS_PTR(rp + (((dbase / 16 + dt) ^ sw) * 16)))));
+        }
+    };
+    // P of tile j (weighted by 2^(m_q - m_ref) while a quarter's maximum
+    // differs from the reference, O rescaled when the reference moves), the
+    // denominator from the operand (wave 4), then the product over the
+    // wave's dims
+    auto pv = [&](int j) {
+        const int ppar = j & 1;
+        const float *mq_lds = reinterpret_cast<const float *>(lds + L::kOffMq + ppar * L::kMqBytes);
+        const uint8_t *p_lds = lds + L::kOffP + ppar * L::kPBytes;
+        f16x8 bp[2][2];
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++)
+                bp[nt][ks] = *reinterpret_cast<const f16x8 *>(p_lds + p_off(nt * 16 + c, 4 * ks + g));
+        bool uneven = false;
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++)
+            uneven |= *reinterpret_cast<const uint32_t *>(
+                          lds + L::kOffFlags + ppar * kHB * 4 + (nt * 16 + c) * 4) != 0x01010101u;
+        if (__ballot(uneven) != 0) {
+            bool any_resc = false;
+            float alpha[2], fq[2][2];
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++) {
+                const float *mrow = mq_lds + (nt * 16 + c) * 4;
+                const f32x4 mq = *reinterpret_cast<const f32x4 *>(mrow);
+                const float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+                const bool resc = mx > m_ref[nt];
+                alpha[nt] = resc ? __builtin_amdgcn_exp2f(m_ref[nt] - mx) : 1.0f;
+                if (resc) m_ref[nt] = mx;
+                any_resc |= resc;
+                fq[nt][0] = __builtin_amdgcn_exp2f(mrow[g >> 1] - m_ref[nt]);
+                fq[nt][1] = __builtin_amdgcn_exp2f(mrow[2 + (g >> 1)] - m_ref[nt]);
+            }
+            if (__ballot(any_resc)) {
+#pragma unroll
+                for (int nt = 0; nt < 2; nt++) {
+#pragma unroll
+                    for (int dt = 0; dt < kDT; dt++) acc[dt][nt] *= alpha[nt];
+                    lacc[nt] *= alpha[nt];
+                }
+            }
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+                    for (int e = 0; e < 8; e++)
+                        bp[nt][ks][e] = (_Float16)((float)bp[nt][ks][e] * fq[nt][ks]);
+        }
+        if (w == 4) {
+            const f16x8 one = {1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++)
+                    lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(one, bp[nt][ks], lacc[nt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int dt = 0; dt < kDT; dt++) {
+            const f16x8 av0 = e4m3x8_to_f16(tv[0][dt][0], tv[0][dt][1]);
+            const f16x8 av1 = e4m3x8_to_f16(tv[1][dt][0], tv[1][dt][1]);
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++) {
+                acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, bp[nt][0], acc[dt][nt], 0, 0, 0);
+                acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bp[nt][1], acc[dt][nt], 0, 0, 0);
+            }
+        }
+    };
+    barrier_raw();                           // tile 0 and the query copy landed
+    read_tv(0);
+    wait_lgkm0();
+    barrier_raw();                           // (the scoring waves hold the query)
+    for (int k = 0; k < n_tiles; k++) {
+        if (k > 0) {
+            pv(k - 1);
+            read_tv(k);
+        }
+        wait_lgkm0();
+        barrier_raw();
+    }
+    pv(n_tiles - 1);
+
+    // epilogue: wave 4's denominators through LDS, then O / l
+    if (w == 4 && g == 0) {
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++) rl_lds[nt * 16 + c] = lacc[nt][0];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < 2; nt++) {
+        const int hh = nt * 16 + c;
+        const int h = hb * kHB + hh;
+        if (h >= a.H) continue;
+        const float l_tot = rl_lds[hh];
+        const int64_t th = (int64_t)t * a.H + h;
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        if (SPLIT) {
+            const int64_t po = (th * a.n_splits + split) * kD + dbase + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < kDT; dt++)
+                *reinterpret_cast<f32x4 *>(a.ws + po + dt * 16) = acc[dt][nt] * inv;
+            if (w == 4 && g == 0) {
+                float *ml = a.ws + (int64_t)a.T * a.H * a.n_splits * kD + (th * a.n_splits + split) * 2;
+                ml[0] = m_ref[nt];
+                ml[1] = l_tot;
+            }
+        } else {
+            const int64_t base = th * kD + dbase + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < kDT; dt++) {
+                const f32x4 o = acc[dt][nt] * inv;
+                if (OUT_BF16) {
+                    u32x2 pk = {f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
+                                f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16)};
+                    *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + base + dt * 16) = pk;
+                } else {
+                    *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + base + dt * 16) = o;
+                }
+            }
+            if (a.lse && w == 4 && g == 0)
+                a.lse[th] = l_tot > 0.0f ? (m_ref[nt] + log2f(l_tot)) * kLn2 : -INFINITY;
+        }
+    }
+}
+
 // Merge of the split partial states: one wavefront per (token, head), each
 // lane owning 8 of the 512 dims.  A split holds its normalised output o_s
 // (fp32) and (m_s, l_s); the merge is
@@ -1409,16 +1866,30 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
     constexpr int kHB = 16 * NT;
     const int n_hb = (a.H + kHB - 1) / kHB;
     const dim3 grid((unsigned)(((int64_t)a.T + 7) / 8 * 8 * n_hb * a.n_splits));
-    constexpr int bytes = Lds<NT, LAYOUT>::kBytes;
-    if (a.n_splits > 1) {
-        constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, true, NT>;
-        allow_big_lds<kern>(bytes);
-        kern<<<grid, dim3(kThreads), bytes, stream>>>(a);
-        launch_combine_s<OUT_BF16>(a, stream);
+    if constexpr (LAYOUT == 0 && QFP8 && NT == 2) {
+        // FP8 query over raw rows in 32-head blocks: the eight-wave kernel
+        if (a.n_splits > 1) {
+            constexpr auto kern = attn_q8_kernel<OUT_BF16, true>;
+            allow_big_lds<kern>(W8::kBytes);
+            kern<<<grid, dim3(W8::kThreads), W8::kBytes, stream>>>(a);
+            launch_combine_s<OUT_BF16>(a, stream);
+        } else {
+            constexpr auto kern = attn_q8_kernel<OUT_BF16, false>;
+            allow_big_lds<kern>(W8::kBytes);
+            kern<<<grid, dim3(W8::kThreads), W8::kBytes, stream>>>(a);
+        }
     } else {
-        constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, false, NT>;
-        allow_big_lds<kern>(bytes);
-        kern<<<grid, dim3(kThreads), bytes, stream>>>(a);
+        constexpr int bytes = Lds<NT, LAYOUT>::kBytes;
+        if (a.n_splits > 1) {
+            constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, true, NT>;
+            allow_big_lds<kern>(bytes);
+            kern<<<grid, dim3(kThreads), bytes, stream>>>(a);
+            launch_combine_s<OUT_BF16>(a, stream);
+        } else {
+            constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, false, NT>;
+            allow_big_lds<kern>(bytes);
+            kern<<<grid, dim3(kThreads), bytes, stream>>>(a);
+        }
     }
     return hipGetLastError();
 }

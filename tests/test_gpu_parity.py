@@ -237,6 +237,38 @@ def test_attention_small(orc, cfg, phase, qfp8, od):
         assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
 
 
+# FP8 query over raw rows with more than 16 heads runs the eight-wavefront
+# kernel (32-head blocks): a prefill list of several 2048-entry splits, a
+# partly filled second head block, a token count that is not a multiple of 8,
+# repeated and padded entries, a token with no valid entry, page size 1.
+Q8_BLOCKS = [
+    dict(seed=221, T=9, H=32, K=2560, layout=W.RAW, seq_len=4000, page_size=64,
+         dup_frac=0.1, neg_frac=0.05, all_masked=(4,)),
+    dict(seed=222, T=5, H=40, K=1152, layout=W.RAW, seq_len=1500, page_size=32),
+    dict(seed=223, T=3, H=32, K=128, layout=W.RAW, seq_len=200, page_size=1, neg_frac=0.4),
+]
+
+
+@pytest.mark.parametrize("cfg", Q8_BLOCKS, ids=[f"s{c['seed']}" for c in Q8_BLOCKS])
+@pytest.mark.parametrize("phase", [0, 1], ids=["decode", "prefill"])
+@pytest.mark.parametrize("od", [dsa.DSA_FP32, dsa.DSA_BF16], ids=["f32", "bf16"])
+def test_fp8_query_32_head_blocks(orc, cfg, phase, od):
+    wl = W.small(**cfg)
+    pool = P.build_pool(orc, wl)
+    di = G.DevInputs(wl)
+    q8_d, sc_d = G.run_quantize(di.q)
+    s_ref = orc.q_scale(wl.q)
+    q8_ref = orc.q_quantize(wl.q, s_ref)
+    assert np.array_equal(G.host(q8_d), q8_ref)
+    ref, ref_lse, ref_err = _oracle_attn(orc, wl, pool, q8_ref, s_ref)
+    out, lse, err = G.run_attn(di, G.dev(pool), phase=phase, out_dtype=od, q=q8_d, q_scale=sc_d)
+    assert err == ref_err
+    G.assert_attn_close(out, ref, od, where=str(cfg))
+    G.assert_lse_close(lse, ref_lse, where=str(cfg))
+    for t in cfg.get("all_masked", ()):
+        assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
+
+
 @pytest.mark.parametrize("H", [16, 32])
 @pytest.mark.parametrize("layout", [W.RAW, W.SCALED, W.ROPE, W.BF16],
                          ids=["raw", "scaled", "rope", "bf16"])
