@@ -12,7 +12,7 @@
 // list (at most 2048 entries).  All heads of the block share every gathered
 // row, so Q.X^T is a real [16NT x 512] x [512 x entries] contraction for the
 // matrix cores, and a row is gathered once per block of up to 32 heads.
-// (An FP8 query in 32-head blocks runs attn_q8_kernel further down: eight
+// (An FP8 query in 32-head blocks runs attn_w8_kernel further down: eight
 // wavefronts of 256 registers, one barrier per tile.)
 //
 //   prologue: the split's indices are resolved once (top-k value -> page
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // overlaps the PV of tile k-1 and each tile's operand reads overlap the
     // phase before.
     static_assert(kParts == 2, "one publishing wave per head tile and quarter");
-    static_assert(!(QFP8 && NT == 2), "FP8 query in 32-head blocks: attn_q8_kernel");
+    static_assert(!(QFP8 && NT == 2), "FP8 query in 32-head blocks: attn_w8_kernel");
     // PV operands read in their own step (one register set; a tile's buffer
     // is refilled right after its step): 32-head blocks and 656-byte rows,
     // whose extra operands would not fit otherwise
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // partial through LDS slot ht*4 + q):
     //   16 heads: wave (q = w & 3, dp = w >> 2) scores quarter q; the dp = 0
     //     waves own their quarter, the dp = 1 waves only publish;
-    //   32 heads, FP8 query: run by attn_q8_kernel (eight waves), not here;
+    //   32 heads, FP8 query: run by attn_w8_kernel (eight waves), not here;
     //   32 heads, bf16 query (kRowPair: the query of both head tiles would
     //     not fit the 128 registers a lane has at 16 waves per CU): wave
     //     (rh = w & 1, dp = (w >> 1) & 1, ht = w >> 2) scores quarters 2rh
@@ -1317,9 +1317,11 @@ struct W8 {
     static_assert(kBytes <= 160 * 1024, "LDS budget");
 };
 
-template <bool OUT_BF16, bool SPLIT>
-__global__ __launch_bounds__(W8::kThreads) void attn_q8_kernel(AttnArgs a) {
+template <bool QFP8, bool OUT_BF16, bool SPLIT>
+__global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
     using L = W8;
+    constexpr int kQRowBytes = QFP8 ? kD : 2 * kD;       // query row bytes
+    constexpr int kQChunks = kQRowBytes / 16;            // 16-byte chunks per head row
     constexpr int kNB = L::kNB, kHB = L::kHB, kDT = L::kDT;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1347,7 +1349,7 @@ __global__ __launch_bounds__(W8::kThreads) void attn_q8_kernel(AttnArgs a) {
     const int seq_len = (a.seq_lens && seq_ok) ? a.seq_lens[seq] : INT_MAX;
     const int begin = split * a.split_len;
     const int n_ent = min(a.K - begin, a.split_len);   // a multiple of 64
-    const float sscale = a.softmax_scale * kLog2e * *a.q_scale;
+    const float sscale = a.softmax_scale * kLog2e * (QFP8 ? *a.q_scale : 1.0f);
 
     // ---- prologue: the split's entries resolved to row sources in LDS (as
     // in attn_kernel: unconditional loads, the page-table row staged when it
@@ -1450,45 +1452,62 @@ __global__ __launch_bounds__(W8::kThreads) void attn_q8_kernel(AttnArgs a) {
         else wait_vm_lgkm0<0>();
     };
 
-    // ---- the query copy (tile buffer 3, chunk k < 64 of head row hl at
+    // ---- the query copy (tile buffer 3, chunk k of head row hl at
     // position k ^ (hl & 7)), issued by the scoring waves before their first
     // tiles, so that the wait for tile 0 covers it
     uint8_t *const qst = lds + 3 * L::kBufBytes;
+    static_assert(kHB * kQRowBytes <= L::kBufBytes, "query copy fits a tile buffer");
     auto q_global = [&](int hl, int byte) {
         const int h = hb * kHB + hl;
-        return reinterpret_cast<const uint8_t *>(a.q) + ((int64_t)t * a.H + (h < a.H ? h : 0)) * kD + byte;
+        return reinterpret_cast<const uint8_t *>(a.q) + ((int64_t)t * a.H + (h < a.H ? h : 0)) * kQRowBytes + byte;
+    };
+    auto q_lds = [&](int hl, int chunk) {
+        return reinterpret_cast<const u32x4 *>(qst + hl * kQRowBytes + ((chunk ^ (hl & 7)) << 4));
     };
 
     if (__builtin_amdgcn_readfirstlane((int)is_v) == 0) {
         // ================= scoring waves =================
         {
+            constexpr int kPerWave = kHB * kQChunks / 4;   // chunks copied by each scoring wave
             const uint32_t qbase = lds_addr(qst);
 #pragma unroll
-            for (int i0 = 0; i0 < kHB * 32 / 4; i0 += 64) {
-                const int i = q * (kHB * 32 / 4) + i0 + lane;
-                const int hl = i / 32, kp = i % 32;
-                dma16(q_global(hl, (kp ^ (hl & 7)) << 4), qbase + (q * (kHB * 32 / 4) + i0) * 16);
+            for (int i0 = 0; i0 < kPerWave; i0 += 64) {
+                const int i = q * kPerWave + i0 + lane;
+                const int hl = i / kQChunks, kp = i % kQChunks;
+                dma16(q_global(hl, (kp ^ (hl & 7)) << 4), qbase + (q * kPerWave + i0) * 16);
             }
         }
         issue_tile8(0);
         if (n_tiles > 1) issue_tile8(1);
         wait_own(0, 1);
         barrier_raw();                       // tile 0 and the query copy landed
-        // the query of both head tiles: bq8[nt][k2] = q8[h][128 k2 + 32 g .. +32]
-        i32x8 bq8[2][4];
+        // The query of both head tiles as the B operand.  FP8:
+        // bq8[nt][k2] = q8[h][128 k2 + 32 g .. +32] (chunks 8 k2 + 2g, +1);
+        // bf16: bq[nt][kk] = q[h][d .. d+8] with d = (4 (kk >> 1) + g) * 16 +
+        // 8 (kk & 1), so that a lane's steps 2m, 2m+1 use the two halves of
+        // one 16-byte row chunk (the reduction index is free: A and B agree).
+        i32x8 bq8[QFP8 ? 2 : 1][QFP8 ? 4 : 1];
+        bf16x8 bq[QFP8 ? 1 : 2][QFP8 ? 1 : 16];
 #pragma unroll
-        for (int nt = 0; nt < 2; nt++)
+        for (int nt = 0; nt < 2; nt++) {
+            const int hl = nt * 16 + c;
+            if constexpr (QFP8) {
 #pragma unroll
-            for (int k2 = 0; k2 < 4; k2++) {
-                const int hl = nt * 16 + c;
-                const int k = 8 * k2 + 2 * g;
-                const u32x4 lo = *reinterpret_cast<const u32x4 *>(qst + hl * kD + ((k ^ (hl & 7)) << 4));
-                const u32x4 hi = *reinterpret_cast<const u32x4 *>(qst + hl * kD + (((k + 1) ^ (hl & 7)) << 4));
-                bq8[nt][k2] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                for (int k2 = 0; k2 < 4; k2++) {
+                    const u32x4 lo = *q_lds(hl, 8 * k2 + 2 * g), hi = *q_lds(hl, 8 * k2 + 2 * g + 1);
+                    bq8[nt][k2] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 16; kk++)
+                    // (bf16 row bytes: chunk 2 d / 16)
+                    bq[nt][kk] = __builtin_bit_cast(bf16x8, *q_lds(hl, ((4 * (kk >> 1) + g) * 16 + 8 * (kk & 1)) / 8));
             }
-        // row chunks of the quarter's row 16q + c: K step k2 takes chunks
-        // 8 k2 + 2g and 8 k2 + 2g + 1
+        }
+        // row chunks of the quarter's row 16q + c: FP8 step k2 takes chunks
+        // 8 k2 + 2g and 8 k2 + 2g + 1, bf16 steps 2m, 2m+1 the halves of
+        // chunk 4m + g
         u32x4 xc[8];
         auto read_xc = [&](int j) {
             const int r = 16 * q + c;
@@ -1496,7 +1515,7 @@ __global__ __launch_bounds__(W8::kThreads) void attn_q8_kernel(AttnArgs a) {
             const int sw = swz<0>(r);
 #pragma unroll
             for (int m = 0; m < 8; m++) {
-                const int ch = (m >> 1) * 8 + g * 2 + (m & 1);
+                const int ch = QFP8 ? (m >> 1) * 8 + g * 2 + (m & 1) : 4 * m + g;
                 xc[m] = *reinterpret_cast<const u32x4 *>(xr + ((ch ^ sw) * 16));
             }
         };
@@ -1515,19 +1534,38 @@ __global__ __launch_bounds__(W8::kThreads) void attn_q8_kernel(AttnArgs a) {
             for (int i = 0; i < L::kLoads; i++) nsrc[i] = row_src(min(nx, n_tiles - 1), i);
             // QK^T of both head tiles over the quarter's 16 entries
             f32x4 part[2];
+            if constexpr (QFP8) {
 #pragma unroll
-            for (int nt = 0; nt < 2; nt++) {
-                f32x4 accg[4];
+                for (int nt = 0; nt < 2; nt++) {
+                    f32x4 accg[4];
 #pragma unroll
-                for (int k2 = 0; k2 < 4; k2++) {
-                    const u32x4 &lo = xc[2 * k2], &hi = xc[2 * k2 + 1];
-                    const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                    accg[k2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        av, bq8[nt][k2], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
+                    for (int k2 = 0; k2 < 4; k2++) {
+                        const u32x4 &lo = xc[2 * k2], &hi = xc[2 * k2 + 1];
+                        const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                        accg[k2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            av, bq8[nt][k2], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; i++) part[nt][i] = (accg[0][i] + accg[1][i]) + (accg[2][i] + accg[3][i]);
+                }
+            } else {
+                // bf16 products of the rows converted FP8 -> bf16 exactly
+                // (each converted operand feeds both head tiles), fp32 sums
+                // in two chains per head tile
+                f32x4 accg[2][2];
+#pragma unroll
+                for (int nt = 0; nt < 2; nt++) accg[nt][0] = accg[nt][1] = f32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int kk = 0; kk < 16; kk++) {
+                    const u32x4 &ch = xc[kk >> 1];
+                    const bf16x8 av = (kk & 1) ? e4m3x8_to_bf16(ch[2], ch[3]) : e4m3x8_to_bf16(ch[0], ch[1]);
+#pragma unroll
+                    for (int nt = 0; nt < 2; nt++)
+                        accg[nt][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[nt][kk], accg[nt][kk & 1], 0, 0, 0);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; i++) part[nt][i] = (accg[0][i] + accg[1][i]) + (accg[2][i] + accg[3][i]);
+                for (int nt = 0; nt < 2; nt++) part[nt] = accg[nt][0] + accg[nt][1];
             }
             // softmax of both head tiles (as attn_kernel's owners): entries
             // 16q + 4g + i of head nt*16 + c
@@ -1866,15 +1904,15 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
     constexpr int kHB = 16 * NT;
     const int n_hb = (a.H + kHB - 1) / kHB;
     const dim3 grid((unsigned)(((int64_t)a.T + 7) / 8 * 8 * n_hb * a.n_splits));
-    if constexpr (LAYOUT == 0 && QFP8 && NT == 2) {
-        // FP8 query over raw rows in 32-head blocks: the eight-wave kernel
+    if constexpr (LAYOUT == 0 && NT == 2) {
+        // raw rows in 32-head blocks: the eight-wave kernel
         if (a.n_splits > 1) {
-            constexpr auto kern = attn_q8_kernel<OUT_BF16, true>;
+            constexpr auto kern = attn_w8_kernel<QFP8, OUT_BF16, true>;
             allow_big_lds<kern>(W8::kBytes);
             kern<<<grid, dim3(W8::kThreads), W8::kBytes, stream>>>(a);
             launch_combine_s<OUT_BF16>(a, stream);
         } else {
-            constexpr auto kern = attn_q8_kernel<OUT_BF16, false>;
+            constexpr auto kern = attn_w8_kernel<QFP8, OUT_BF16, false>;
             allow_big_lds<kern>(W8::kBytes);
             kern<<<grid, dim3(W8::kThreads), W8::kBytes, stream>>>(a);
         }
