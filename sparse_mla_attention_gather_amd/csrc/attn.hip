@@ -7,13 +7,15 @@
 // and value.  out[t,h] = softmax_j(scale * <q[t,h], x_j>) . x_j over the
 // multiset of valid entries; all-masked tokens give 0 (lse = -inf).
 //
-// Work decomposition: one workgroup (16 wavefronts, 4 per SIMD) owns one unit
-// = (token t, block of 16 NT heads, NT = 1 or 2) and one split of t's top-k
-// list (at most 2048 entries).  All heads of the block share every gathered
-// row, so Q.X^T is a real [16NT x 512] x [512 x entries] contraction for the
-// matrix cores, and a row is gathered once per block of up to 32 heads.
-// (An FP8 query in 32-head blocks runs attn_w8_kernel further down: eight
-// wavefronts of 256 registers, one barrier per tile.)
+// Work decomposition: one workgroup owns one unit = (token t, block of heads)
+// and one split of t's top-k list (at most 2048 entries).  All heads of the
+// block share every gathered row, so Q.X^T is a real [heads x 512] x
+// [512 x entries] contraction for the matrix cores, and a row is gathered
+// once per block.  attn_kernel (16 wavefronts, 4 per SIMD, 128 registers)
+// takes blocks of 16 heads, for every row layout; attn_w8_kernel further
+// down (8 wavefronts, 256 registers) takes blocks of 32 heads over raw rows,
+// the form used when there are more than 16 heads.  The outline below is
+// attn_kernel's.
 //
 //   prologue: the split's indices are resolved once (top-k value -> page
 //     table -> slot; -1 for padding and for invalid values, which are also
@@ -95,17 +97,17 @@ constexpr float kNoMax = -1.0e30f;
 // add a ring of RoPE parts (64 rows x 128 B per tile) and, to stay within the
 // 160 KB of a CU, keep three tile buffers instead of four; 1024-byte bf16
 // rows keep two buffers of 64 KB.
-template <int NT, int LAYOUT>
+template <int LAYOUT>
 struct Lds {
-    static constexpr int kHB = 16 * NT;
+    static constexpr int kHB = 16;
     static constexpr int kNB = LAYOUT == 2 ? 3 : LAYOUT == 3 ? 2 : kNBuf;   // tile buffers
     static constexpr int kParts = 2;                             // QK dim parts
     static constexpr int kRowPitch = LAYOUT == 3 ? 1024 : 512;   // LDS bytes per row
     static constexpr int kBufBytes = kTile * kRowPitch;          // 32 KB (bf16 rows: 64 KB)
     static constexpr bool kHasScales = LAYOUT == 1 || LAYOUT == 2;
-    // raw FP8 rows in 16-head blocks carry P to the PV product as two f16
-    // terms (hi + lo), see the softmax
-    static constexpr bool kLo = LAYOUT == 0 && NT == 1;
+    // raw FP8 rows carry P to the PV product as two f16 terms (hi + lo),
+    // see the softmax
+    static constexpr bool kLo = LAYOUT == 0;
     static constexpr int kScBytes = kTile * 16;                  // 1 KB scales
     static constexpr int kRopeTile = kTile * 2 * kRopeDim;       // 8 KB RoPE parts
     static constexpr int kOffScales = kNB * kBufBytes;
@@ -113,7 +115,7 @@ struct Lds {
     static constexpr int kOffSlots = kOffScales + (kHasScales ? kNScale * kScBytes : 0);
     // partial S^T of the waves holding dim parts 1.. (16 x 16 fp32 each)
     static constexpr int kOffSp = kOffSlots + kMaxSplit * 8;
-    static constexpr int kSpBytes = NT * (kParts - 1) * 4 * 1024;
+    static constexpr int kSpBytes = (kParts - 1) * 4 * 1024;
     // P ([kHB][64] 16-bit, swizzled; the lo terms follow the hi terms): one
     // buffer, since the PV waves hold tile k's P in registers before the
     // barrier after which the owners write tile k+1's; then the quarter
@@ -287,10 +289,10 @@ __device__ __forceinline__ TileSlots read_slots(const uint64_t *slots, int tile_
 // 16-byte scale words; 656-byte rows one 32-lane instruction for their RoPE
 // parts (lane l -> row 4w + (l >> 3), position l & 7 of the row's 128 bytes
 // in ring slot `buf`, holding chunk (l & 7) ^ swz<LAYOUT>(row)).
-template <int LAYOUT, int NT>
+template <int LAYOUT>
 __device__ __forceinline__ void issue_tile(uint32_t lds0, const TileSlots &s,
                                            int buf, int sbuf, int w, int lane) {
-    using L = Lds<NT, LAYOUT>;
+    using L = Lds<LAYOUT>;
     const int r0 = kRowsPerWave * w;
     const uint32_t dst = lds0 + buf * L::kBufBytes + r0 * L::kRowPitch;
     // (a masked entry's source is its zero row of kZeroRow)
@@ -326,9 +328,10 @@ __device__ __forceinline__ void issue_tile(uint32_t lds0, const TileSlots &s,
     }
 }
 
-template <int LAYOUT, bool QFP8, bool OUT_BF16, bool SPLIT, int NT>
+template <int LAYOUT, bool QFP8, bool OUT_BF16, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
-    using L = Lds<NT, LAYOUT>;
+    using L = Lds<LAYOUT>;
+    constexpr int NT = 1;                        // head tiles of 16 per block
     constexpr int kNB = L::kNB;                  // tile buffers
     constexpr int kHB = L::kHB;
     constexpr int kParts = L::kParts;            // dim parts of the QK reduction
@@ -342,12 +345,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     // accumulate PV one tile behind, so the owners' softmax of tile k
     // overlaps the PV of tile k-1 and each tile's operand reads overlap the
     // phase before.
-    static_assert(kParts == 2, "one publishing wave per head tile and quarter");
-    static_assert(!(QFP8 && NT == 2), "FP8 query in 32-head blocks: attn_w8_kernel");
+    static_assert(kParts == 2, "one publishing wave per quarter");
     // PV operands read in their own step (one register set; a tile's buffer
-    // is refilled right after its step): 32-head blocks and 656-byte rows,
-    // whose extra operands would not fit otherwise
-    constexpr bool kLate = NT == 2 || LAYOUT >= 2;
+    // is refilled right after its step): 656-byte and bf16 rows, whose extra
+    // operands would not fit otherwise
+    constexpr bool kLate = LAYOUT >= 2;
     constexpr bool kScaled = LAYOUT == 1 || LAYOUT == 2;   // rows carry group scales
     constexpr int kDT = 4;                       // PV: 16-dim tiles per wave
     // tiles requested before the first lands (1 to 4 measured the same)
@@ -359,29 +361,20 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15, g = lane >> 4;
     const bool is_v = w >= 8;                    // a PV-only wave
-    // Scoring (partials of 16 entries x 16 heads x one 256-dim part dp;
-    // entry quarter q and head tile ht are owned -- parts added, P formed --
-    // by one wave, to which the wave holding the other part publishes its
-    // partial through LDS slot ht*4 + q):
-    //   16 heads: wave (q = w & 3, dp = w >> 2) scores quarter q; the dp = 0
-    //     waves own their quarter, the dp = 1 waves only publish;
-    //   32 heads, FP8 query: run by attn_w8_kernel (eight waves), not here;
-    //   32 heads, bf16 query (kRowPair: the query of both head tiles would
-    //     not fit the 128 registers a lane has at 16 waves per CU): wave
-    //     (rh = w & 1, dp = (w >> 1) & 1, ht = w >> 2) scores quarters 2rh
-    //     and 2rh + 1 of head tile ht and owns quarter 2rh + dp.
-    constexpr bool kRowPair = NT == 2 && !QFP8;
+    // Scoring (partials of 16 entries x 16 heads x one 256-dim part dp):
+    // wave (q = w & 3, dp = w >> 2) scores entry quarter q; the dp = 0 waves
+    // own their quarter (add the other part, form P), the dp = 1 waves only
+    // publish their partial, through LDS slot q.  (32-head blocks run
+    // attn_w8_kernel.)
     // scoring waves read a tile's row chunks in the tile's own step rather
     // than during the softmax before (possible with kLate's buffer rotation)
-    constexpr bool kOwnStep = kRowPair || LAYOUT >= 2;
-    constexpr int kRT = kRowPair ? 2 : 1;        // entry quarters a scoring wave scores
-    constexpr int kQT = kRowPair ? 1 : NT;       // head tiles it scores
-    const int rh = w & 1;
-    const int dp = kRowPair ? (w >> 1) & 1 : (w >> 2) % kParts;      // QK: dims part
-    const int wq = kRowPair ? 2 * rh + dp : w & 3;   // entry quarter owned (and scored)
-    const int ht = kRowPair ? (w >> 2) & 1 : (NT == 1 ? 0 : dp);
-    // (owns: the ownership of a scoring wave, a constant with 32 heads)
-    const bool owns = kRowPair || NT == 2 || dp == 0;
+    constexpr bool kOwnStep = LAYOUT >= 2;
+    constexpr int kRT = 1;                       // entry quarters a scoring wave scores
+    constexpr int kQT = NT;                      // head tiles it scores
+    const int dp = (w >> 2) % kParts;            // QK: dims part
+    const int wq = w & 3;                        // entry quarter owned (and scored)
+    const int ht = 0;
+    const bool owns = dp == 0;
     const bool owner = !is_v && owns;
     const int dbase = 64 * (w - 8);              // PV: first of this wave's dims
     const int n_hb = (a.H + kHB - 1) / kHB;
@@ -426,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     auto load_q = [&](auto at) {
 #pragma unroll
         for (int nt = 0; nt < kQT; nt++) {
-            const int hl = (kRowPair ? ht : nt) * 16 + c;
+            const int hl = nt * 16 + c;
             if constexpr (LAYOUT == 2)
                 bqr = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(at(hl, (kD + dp * 32 + g * 8) * 2)));
             if constexpr (QFP8) {
@@ -576,14 +569,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < kFill0; i++)
         if (i < n_tiles)
-            issue_tile<LAYOUT, NT>(lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
+            issue_tile<LAYOUT>(lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
                                    i, w, lane);
     auto fill_rest = [&](auto last) {
         constexpr bool LAST = decltype(last)::value;
 #pragma unroll
         for (int i = kFill0; i < kNB; i++)
             if (i < n_tiles && (i == kNB - 1) == LAST)
-                issue_tile<LAYOUT, NT>(lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
+                issue_tile<LAYOUT>(lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
                                        i, w, lane);
     };
 
@@ -599,8 +592,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     float m_ref[NT];
     float s_run = 0.0f, s_ref = 0.0f;
     f32x4 acc[kDT][NT];
-    // One-term f16 P (raw rows in 32-head blocks, group-scaled rows): PV
-    // wave 8 accumulates the denominator itself, as the product of a ones
+    // One-term f16 P (group-scaled rows): PV wave 8 accumulates the
+    // denominator itself, as the product of a ones
     // operand with the very P operand of the numerator (same roundings,
     // same rescales), so that the rounding of an entry's weight moves
     // numerator and denominator alike.  (bf16 rows, whose kernel has no
@@ -639,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     auto read_xc = [&](int j) {
 #pragma unroll
         for (int rt = 0; rt < kRT; rt++) {
-            const int r = 16 * (kRowPair ? 2 * rh + rt : wq) + c;
+            const int r = 16 * wq + c;
             const uint8_t *xr = lds + (j % kNB) * L::kBufBytes + r * L::kRowPitch;
             const int sw = swz<LAYOUT>(r);
 #pragma unroll
@@ -794,8 +787,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         for (int rt = 0; rt < kRT; rt++)
 #pragma unroll
             for (int nt = 0; nt < kQT; nt++) {
-                const int qt = kRowPair ? ht : nt;         // its head tile
-                const int qq = kRowPair ? 2 * rh + rt : wq;        // its entry quarter
+                const int qt = nt;                         // its head tile
+                const int qq = wq;                         // its entry quarter
                 if (!(owner && qt == ht && qq == wq)) {
                     const int slot = qt * 4 + qq;
                     *reinterpret_cast<f32x4 *>(sp_lds + (slot * 16 + c) * 16 + 4 * sp_slot(g, c)) =
@@ -822,8 +815,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         // own part of the owned (quarter, head tile) plus the other part's,
         // published
         f32x4 s;
-        if constexpr (kRowPair) s = dp == 0 ? part[0] : part[1];
-        else s = (kQT == 1 || ht == 0) ? part[0] : part[kQT - 1];
+        s = part[0];
         {
             const int slot = ht * 4 + wq;
             s += *reinterpret_cast<const f32x4 *>(sp_lds + (slot * 16 + c) * 16 + 4 * sp_slot(g, c));
@@ -862,16 +854,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_own);   // masked: 2^-inf = 0
         // P goes to the PV product as 16-bit values.  Raw FP8 rows (whose
-        // values reach +-448) in 16-head blocks carry it as two f16 terms,
-        // hi = f16(P) and lo = f16(P - hi): one f16 rounding alone (2^-11
-        // relative) moves a weighted sum of such values by up to 2^-10 of
-        // its spread; the owners' shares of the denominator are then sums
-        // of P itself.  Everything else carries one term (f16; bf16 for
-        // bf16 rows, whose PV product takes bf16): in 32-head blocks a
-        // second term would double the PV waves' matrix work, which sets
-        // their pace.  The denominator of one-term P is formed from the
-        // operand itself in the PV waves (lacc); bf16 rows sum it here as
-        // rounded.
+        // values reach +-448) carry it as two f16 terms, hi = f16(P) and
+        // lo = f16(P - hi): one f16 rounding alone (2^-11 relative) moves a
+        // weighted sum of such values by up to 2^-10 of its spread; the
+        // owners' shares of the denominator are then sums of P itself.
+        // Group-scaled rows carry one f16 term (the entry's scale factor
+        // multiplies it in the PV waves), whose denominator is formed from
+        // the operand itself in the PV waves (lacc); bf16 rows carry one
+        // bf16 term (their PV product takes bf16) and sum it here as
+        // rounded.  (32-head blocks: attn_w8_kernel, one f16 term.)
         const int poff = p_off(hh, 2 * wq + (g >> 1)) + (g & 1) * 8;
         if constexpr (LAYOUT == 3) {
             uint32_t b[4];
@@ -1179,15 +1170,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         //   k+1's transpose operands into tv[PAR^1];  barrier;
         //   tile k+1's buffer takes tile k+1+kNBuf.
         // Both roles pass the same barriers in the same order.
-        // 32 heads (kLate): the PV waves read tile k's transpose operands in
-        // step k itself, into a single register set, and tile k's buffer
-        // (not tile k+1's) takes the next tile after step k, so that kNBuf - 1
-        // tiles rather than kNBuf are in flight beyond the one being scored.
+        // 656-byte and bf16 rows (kLate): the PV waves read tile k's
+        // transpose operands in step k itself, into a single register set,
+        // and tile k's buffer (not tile k+1's) takes the next tile after
+        // step k, so that one tile fewer is in flight beyond the one being
+        // scored.
         constexpr int kAhead = kLate ? kNB - 1 : kNB;
         auto refill = [&](int k, const TileSlots &nsl) {
             const int nx = k + 1 + kAhead;
             if (nx < n_tiles)
-                issue_tile<LAYOUT, NT>(lds0, nsl, nx % kNB, nx % kNScale, w, lane);
+                issue_tile<LAYOUT>(lds0, nsl, nx % kNB, nx % kNScale, w, lane);
         };
         // tile 0's operands, then (16 heads) its buffer takes tile kNBuf
         // (each role keeps its own registers: nothing flows from one role's
@@ -1209,7 +1201,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             barrier_raw();
             // every wave holds its query: its buffer takes its tile
             if constexpr (kStageQ) fill_rest(std::true_type{});
-            if (!kLate && kNB < n_tiles) issue_tile<LAYOUT, NT>(lds0, nsl, 0, kNB % kNScale, w, lane);
+            if (!kLate && kNB < n_tiles) issue_tile<LAYOUT>(lds0, nsl, 0, kNB % kNScale, w, lane);
         };
         // (the role test goes through readfirstlane so that the compiler
         // sees a uniform branch and gives each role its own registers)
@@ -1273,16 +1265,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     }
 }
 // ===========================================================================
-// FP8 query over raw rows in 32-head blocks: eight wavefronts of 256
-// registers (two per SIMD) instead of sixteen of 128.
+// Raw rows in 32-head blocks: eight wavefronts of 256 registers (two per
+// SIMD) instead of sixteen of 128.
 //
-// The sixteen-wave kernel above splits a 32-head block's QK^T over two
-// 256-dim halves, whose partial scores cross waves through LDS, and has each
-// of its eight PV waves read all of P: about 150 KB of LDS traffic per
-// 64-entry tile, which sets its pace.  With 256 registers a lane:
+// Sixteen waves of 128 registers cannot hold a 32-head block's query over
+// all dims: their scoring splits QK^T over two 256-dim halves, whose partial
+// scores cross waves through LDS, and each of their eight PV waves reads all
+// of P; about 150 KB of LDS traffic per 64-entry tile set the pace of that
+// form.  With 256 registers a lane:
 //   waves 0-3 (scoring, entry quarter q = w) hold the query of both head
-//     tiles over all 512 dims and score their quarter completely (eight FP8
-//     MFMAs per tile), then run the softmax of both head tiles.  They also
+//     tiles over all 512 dims and score their quarter completely (FP8
+//     query: eight FP8 MFMAs per tile; bf16 query: each row chunk converted
+//     once and fed to both head tiles' bf16 MFMAs), then run the softmax of
+//     both head tiles.  They also
 //     copy their own quarter's 16 rows of every tile, so that each waits for
 //     its rows with vmcnt alone and reads the next tile's row chunks during
 //     the softmax, with no barrier in between;
@@ -1293,9 +1288,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 // k+1 before barrier k, so the PV waves read that tile after it; P, the
 // quarter maxima and the flags are double-buffered by tile parity.  LDS
 // traffic per tile: DMA 32 KB, row chunks 32 KB, P 4 + 16 KB, transpose
-// operands 32 KB.  Numerics are those of the sixteen-wave kernel (the same
-// products, the same lazy maximum, one f16 term of P, the denominator from
-// the P operand itself).
+// operands 32 KB.  Numerics: attn_kernel's products and lazy maximum; P as
+// one f16 term (a second would double the PV waves' matrix work, which sets
+// their pace), with the denominator formed from that operand itself, so
+// that the rounding of an entry's weight moves numerator and denominator
+// alike.
 struct W8 {
     static constexpr int kWaves = 8;
     static constexpr int kThreads = 64 * kWaves;
@@ -1917,14 +1914,15 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
             kern<<<grid, dim3(W8::kThreads), W8::kBytes, stream>>>(a);
         }
     } else {
-        constexpr int bytes = Lds<NT, LAYOUT>::kBytes;
+        static_assert(NT == 1, "16-head blocks");
+        constexpr int bytes = Lds<LAYOUT>::kBytes;
         if (a.n_splits > 1) {
-            constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, true, NT>;
+            constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, true>;
             allow_big_lds<kern>(bytes);
             kern<<<grid, dim3(kThreads), bytes, stream>>>(a);
             launch_combine_s<OUT_BF16>(a, stream);
         } else {
-            constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, false, NT>;
+            constexpr auto kern = attn_kernel<LAYOUT, QFP8, OUT_BF16, false>;
             allow_big_lds<kern>(bytes);
             kern<<<grid, dim3(kThreads), bytes, stream>>>(a);
         }
