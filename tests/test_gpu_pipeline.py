@@ -6,7 +6,8 @@
   top-k indices have been changed in place; every replay is compared with the
   oracle ("[DSA] Support group-scaled FP8 NoPE KV reads for CUDA TileLang",
   Accuracy Tests: graph replay with changing indices, queries and scale
-  data).  Eager work and synchronisations run between the replays.
+  data).  Eager work and synchronisations run between the replays.  16 and
+  32 heads (the 16- and 32-head block forms of the attention).
 * Context-parallel merge on one GPU: the pages name an attention
   context-parallel split whose partial results are merged by their
   log-sum-exp ("extend CUDA TileLang raw FP8 KV path", Modifications, where
@@ -35,8 +36,10 @@ def _gpu():
 
 
 @pytest.mark.parametrize("given_scale", [False, True], ids=["amax_scale", "given_scale"])
-def test_graph_replay_prefill_pipeline(orc, given_scale):
-    prefix, T, H, K = 200, 300, 16, 256
+@pytest.mark.parametrize("H", [16, 32], ids=["h16", "h32"])
+def test_graph_replay_prefill_pipeline(orc, given_scale, H):
+    # (32 heads: the 32-head block form of the attention)
+    prefix, T, K = 200, 300, 256
     wl = W.q8_prefill(seed=45, prefix=prefix, T=T, H=H, K=K, num_slots=1 << 14)
     print(f"graph replay prefill pipeline: T={T} H={H} K={K} given_scale={given_scale}",
           flush=True)
@@ -134,8 +137,9 @@ def _lse_merge(outs, lses):
 
 @pytest.mark.parametrize("layout", [W.RAW, W.SCALED], ids=["raw", "scaled"])
 @pytest.mark.parametrize("n", [2, 3])
-def test_context_parallel_lse_merge(orc, layout, n):
-    wl = W.small(601 + n, T=6, H=16, K=1024, layout=layout, seq_len=3000, page_size=64,
+@pytest.mark.parametrize("H", [16, 32], ids=["h16", "h32"])
+def test_context_parallel_lse_merge(orc, layout, n, H):
+    wl = W.small(601 + n, T=6, H=H, K=1024, layout=layout, seq_len=3000, page_size=64,
                  all_masked=(4,))
     pool = P.build_pool(orc, wl)
     pool_d = G.dev(pool)
