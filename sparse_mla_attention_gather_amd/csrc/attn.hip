@@ -1277,10 +1277,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 //     tiles over all 512 dims and score their quarter completely (FP8
 //     query: eight FP8 MFMAs per tile; bf16 query: each row chunk converted
 //     once and fed to both head tiles' bf16 MFMAs), then run the softmax of
-//     both head tiles.  They also
-//     copy their own quarter's 16 rows of every tile, so that each waits for
-//     its rows with vmcnt alone and reads the next tile's row chunks during
-//     the softmax, with no barrier in between;
+//     both head tiles.  They also copy their own quarter's 16 rows of every
+//     tile, so that each waits for its rows with vmcnt alone and reads the
+//     next tile's row chunks during the softmax, with no barrier in between;
 //   waves 4-7 (PV, dims 128 (w - 4) .. +128) accumulate both head tiles one
 //     tile behind: P of tile k-1 and the transpose operands read in step
 //     k-1, then tile k's operands.
