@@ -240,14 +240,33 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // lds_base + 16 l.  Issued through inline assembly so that the compiler does
 // not see pending LDS writes: it would otherwise guard every later LDS read
 // with a wait for all outstanding loads.  Completion is tracked explicitly
-// with s_waitcnt vmcnt before the barrier that publishes a tile.
+// with s_waitcnt vmcnt before the barrier that publishes a tile.  The
+// compiler's hazard checks do not look inside an asm block, so the block
+// carries the wait state that an LDS DMA needs after a scalar write of M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved; only this asm writes it
 __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(gptr), "s"(lds_base) : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// A 16- or 8-byte global store written through to device scope (sc1), so
+// that the line is not left dirty in this XCD's L2 for the write-back that
+// ends the kernel; the decode's split partials otherwise put that write-back
+// between the attention kernel and the merge.  A cache policy only: the
+// kernel boundary still orders the data for its reader.  The trailing s_nop
+// is the wait state a vector store of more than 8 bytes needs before a
+// vector instruction may overwrite its data registers (the compiler's hazard
+// checks do not see a store inside an asm block).
+template <typename V>
+__device__ __forceinline__ void store_through(V *p, V v) {
+    static_assert(sizeof(V) == 16 || sizeof(V) == 8, "dwordx4 or dwordx2");
+    if constexpr (sizeof(V) == 16)
+        asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
+    else
+        asm volatile("global_store_dwordx2 %0, %1, off sc1\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
+}
 
 // Bytes of one pool row of a layout.
 template <int LAYOUT>
@@ -1129,7 +1148,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 const int64_t po = (th * a.n_splits + split) * kD + dbase + 4 * g;
 #pragma unroll
                 for (int dt = 0; dt < kDT; dt++)
-                    *reinterpret_cast<f32x4 *>(a.ws + po + dt * 16) = acc[dt][nt] * inv;
+                    store_through(reinterpret_cast<f32x4 *>(a.ws + po + dt * 16), acc[dt][nt] * inv);
                 if (w == w_first && g == 0) {
                     float *ml = a.ws + (int64_t)a.T * a.H * a.n_splits * kD +
                                 (th * a.n_splits + split) * 2;
@@ -1739,7 +1758,7 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
             const int64_t po = (th * a.n_splits + split) * kD + dbase + 4 * g;
 #pragma unroll
             for (int dt = 0; dt < kDT; dt++)
-                *reinterpret_cast<f32x4 *>(a.ws + po + dt * 16) = acc[dt][nt] * inv;
+                store_through(reinterpret_cast<f32x4 *>(a.ws + po + dt * 16), acc[dt][nt] * inv);
             if (w == 4 && g == 0) {
                 float *ml = a.ws + (int64_t)a.T * a.H * a.n_splits * kD + (th * a.n_splits + split) * 2;
                 ml[0] = m_ref[nt];
