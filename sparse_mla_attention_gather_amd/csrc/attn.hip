@@ -70,7 +70,14 @@
 
 #include <type_traits>
 
+// This file is compiled without NaN semantics (-fno-honor-nans): its scores
+// are finite, -inf for masked entries, and the running maxima start at the
+// finite kNoMax, so maxima need no NaN quieting.  The encoders in common.h,
+// which test for NaN, are not used here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wnan-infinity-disabled"
 #include "common.h"
+#pragma clang diagnostic pop
 #include "launch.h"
 
 namespace dsa {
