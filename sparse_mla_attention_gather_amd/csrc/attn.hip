@@ -118,7 +118,7 @@ struct Lds {
     static constexpr int kScBytes = kTile * 16;                  // 1 KB scales
     static constexpr int kRopeTile = kTile * 2 * kRopeDim;       // 8 KB RoPE parts
     static constexpr int kOffScales = kNB * kBufBytes;
-    // the entries' row sources (64-bit addresses, see kMaskedBit)
+    // the entries' row sources (64-bit addresses, see kMaskBits)
     static constexpr int kOffSlots = kOffScales + (kHasScales ? kNScale * kScBytes : 0);
     // partial S^T of the waves holding dim parts 1.. (16 x 16 fp32 each)
     static constexpr int kOffSp = kOffSlots + kMaxSplit * 8;
@@ -199,6 +199,18 @@ __device__ __forceinline__ float max_over_g(float v) {
     v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// The maxima over g of two values at once: the first swap pairs the lanes
+// l, l ^ 32 of a in lanes 0-31 and those of b in lanes 32-63, the second the
+// 16-lane rows, the third hands every lane both results.
+__device__ __forceinline__ void max_over_g2(float &a, float &b) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    float v = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+    const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+    const auto u = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    a = __uint_as_float(u[0]);
+    b = __uint_as_float(u[1]);
 }
 __device__ __forceinline__ float sum_over_g(float v) {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -283,9 +295,13 @@ constexpr int64_t row_bytes() {
 
 // An entry's row source, resolved once in the prologue: the row's address in
 // the pool, or for a masked entry the address of zero row (entry mod 64) of
-// kZeroRow with bit 63 set (the mark of a masked entry; cleared before use).
-// The tile DMA then forms each lane's address with two instructions.
-constexpr uint64_t kMaskedBit = 1ull << 63;
+// kZeroRow with the bits of an fp32 -inf (0xff800000) or-ed into its high
+// word (cleared before use; the launcher checks that no pool address has any
+// of them set).  The tile DMA then forms each lane's address with two
+// instructions, and the softmax takes the mask term of a score (0 or -inf)
+// as the high word of the source with one AND.
+constexpr uint64_t kMaskBits = 0xff800000ull << 32;
+__device__ __forceinline__ float mask_term(int32_t src_hi) { return __int_as_float(src_hi & (int32_t)0xff800000u); }
 
 // Row sources of the rows this wave copies for one tile (see issue_tile).
 struct TileSlots {
@@ -323,7 +339,7 @@ __device__ __forceinline__ void issue_tile(uint32_t lds0, const TileSlots &s,
     const uint32_t dst = lds0 + buf * L::kBufBytes + r0 * L::kRowPitch;
     // (a masked entry's source is its zero row of kZeroRow)
     auto src_of = [](uint64_t src, int byte) {
-        return reinterpret_cast<const uint8_t *>((src & ~kMaskedBit) + (uint64_t)byte);
+        return reinterpret_cast<const uint8_t *>((src & ~kMaskBits) + (uint64_t)byte);
     };
     if constexpr (LAYOUT == 3) {
         // one 1024-byte row per instruction: lane l -> position l, holding
@@ -550,7 +566,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(err));   // the wave's
             if (j < n_ent)
                 slots[j] = s >= 0 ? reinterpret_cast<uint64_t>(a.pool + (int64_t)s * row_bytes<LAYOUT>())
-                                  : reinterpret_cast<uint64_t>(kZeroRow + (j & (kTile - 1)) * row_bytes<LAYOUT>()) | kMaskedBit;
+                                  : reinterpret_cast<uint64_t>(kZeroRow + (j & (kTile - 1)) * row_bytes<LAYOUT>()) | kMaskBits;
             const uint64_t vb = __builtin_amdgcn_ballot_w64(j < n_ent && s >= 0);
             if (vb) last = max(last, w * 64 + 63 - (int)__builtin_clzll(vb) + i * kThreads);
         }
@@ -734,7 +750,25 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 for (int jj = 0; jj < kGpp; jj++)
                     scv[i][jj] = scf[(16 * wq + 4 * g + i) * 4 + dp * kGpp + jj];
         }
-        if constexpr (QFP8) {
+        if constexpr (QFP8 && !kScaled) {
+            // raw rows: one chain through the accumulator input (exact fp32
+            // addition of C, as in attn_w8_kernel)
+#pragma unroll
+            for (int nt = 0; nt < kQT; nt++) {
+                f32x4 acc8 = {0, 0, 0, 0};
+#pragma unroll
+                for (int k2 = 0; k2 < kSteps8; k2++) {
+                    const u32x4 &lo = xc[0][2 * k2], &hi = xc[0][2 * k2 + 1];
+                    const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    acc8 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        av, bq8[nt][k2], acc8, 0, 0, 0, 127, 0, 127);
+                }
+                part[nt] = acc8;
+            }
+        } else if constexpr (QFP8) {
+            // group-scaled rows: each 128-wide step is scaled by its group's
+            // scale, so the steps are summed apart
 #pragma unroll
             for (int nt = 0; nt < kQT; nt++) {
                 f32x4 accg[kSteps8];
@@ -748,10 +782,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 }
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    float s = !kScaled ? accg[0][i] : accg[0][i] * scv[i][0];
+                    float s = accg[0][i] * scv[i][0];
 #pragma unroll
-                    for (int k2 = 1; k2 < kSteps8; k2++)
-                        s += !kScaled ? accg[k2][i] : accg[k2][i] * scv[i][k2];
+                    for (int k2 = 1; k2 < kSteps8; k2++) s += accg[k2][i] * scv[i][k2];
                     part[nt][i] = s;
                 }
             }
@@ -835,7 +868,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         float *mq_w = reinterpret_cast<float *>(lds + L::kOffMq + par * L::kMqBytes);
         uint8_t *p_w = lds + L::kOffP;
         const int hh = ht * 16 + c;
-        // (the high words of the entries' row sources: negative when masked)
+        // (the high words of the entries' row sources, see kMaskBits)
         const int32_t *slh = reinterpret_cast<const int32_t *>(slots + j * kTile + 16 * wq + 4 * g) + 1;
         const int4 sl4 = {slh[0], slh[2], slh[4], slh[6]};
         // own part of the owned (quarter, head tile) plus the other part's,
@@ -852,14 +885,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         if constexpr (kScaled)
             sc_own = reinterpret_cast<const float *>(lds + L::kOffScales + (j % kNScale) * L::kScBytes)[lane * 4 + wq];
         then();
-        const int slv[4] = {sl4.x, sl4.y, sl4.z, sl4.w};
-        float sv[4], mx = -INFINITY;
+        // a masked entry reads a zero row: its score is exactly 0, and the
+        // mask term (-inf) masks it
+        const float madd[4] = {mask_term(sl4.x), mask_term(sl4.y), mask_term(sl4.z), mask_term(sl4.w)};
+        float sv[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            sv[i] = slv[i] >= 0 ? s[i] * sscale : -INFINITY;
-            mx = fmaxf(mx, sv[i]);
-        }
-        mx = max_over_g(mx);
+        for (int i = 0; i < 4; i++) sv[i] = __builtin_fmaf(s[i], sscale, madd[i]);
+        const float mx = max_over_g(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
         if (j > 0) {
             // adopt the largest quarter maximum of the previous tile, so that
             // the quarters keep a common reference (their P then needs no
@@ -1428,7 +1460,7 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
             n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(err));   // the wave's
             if (j < n_ent)
                 slots[j] = s >= 0 ? reinterpret_cast<uint64_t>(a.pool + (int64_t)s * kRawBytes)
-                                  : reinterpret_cast<uint64_t>(kZeroRow + (j & (kTile - 1)) * kRawBytes) | kMaskedBit;
+                                  : reinterpret_cast<uint64_t>(kZeroRow + (j & (kTile - 1)) * kRawBytes) | kMaskBits;
             const uint64_t vb = __builtin_amdgcn_ballot_w64(j < n_ent && s >= 0);
             if (vb) last = max(last, w * 64 + 63 - (int)__builtin_clzll(vb) + i * L::kThreads);
         }
@@ -1455,7 +1487,7 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
 #pragma unroll
         for (int k = 0; k < L::kLoads; k++) {
             const int r = 16 * q + 2 * k + (lane >> 5);
-            dma16(reinterpret_cast<const uint8_t *>((src[k] & ~kMaskedBit) + (uint64_t)((pos ^ swz<0>(r)) * 16)),
+            dma16(reinterpret_cast<const uint8_t *>((src[k] & ~kMaskBits) + (uint64_t)((pos ^ swz<0>(r)) * 16)),
                   dst + k * 1024);
         }
     };
@@ -1535,10 +1567,15 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
             const int r = 16 * q + c;
             const uint8_t *xr = lds + (j % kNB) * L::kBufBytes + r * kRawBytes;
             const int sw = swz<0>(r);
+            // chunk ch(m + 4) = ch(m) + 16, and the swizzle (< 16) leaves bit
+            // 4 of a chunk index alone: steps m and m + 4 share an address,
+            // 256 bytes apart
 #pragma unroll
-            for (int m = 0; m < 8; m++) {
+            for (int m = 0; m < 4; m++) {
                 const int ch = QFP8 ? (m >> 1) * 8 + g * 2 + (m & 1) : 4 * m + g;
-                xc[m] = *reinterpret_cast<const u32x4 *>(xr + ((ch ^ sw) * 16));
+                const uint8_t *xa = xr + ((ch ^ sw) * 16);
+                xc[m] = *reinterpret_cast<const u32x4 *>(xa);
+                xc[m + 4] = *reinterpret_cast<const u32x4 *>(xa + 256);
             }
         };
         read_xc(0);
@@ -1548,28 +1585,37 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
         if (n_tiles > 3) issue_tile8(3);
 
         float m_own[2] = {kNoMax, kNoMax};
+        // this lane's LDS addresses in the step, less their per-tile parts
+        // (head tile nt adds 16 heads: 64 bytes of flags and maxima, 2 KB of
+        // P, since the P swizzle (hh >> 1) & 7 does not see nt)
+        const uint64_t *const src_l = slots + 16 * q + (lane >> 5);          // + j kTile + 2 i
+        const int32_t *const mask_l = reinterpret_cast<const int32_t *>(slots + 16 * q + 4 * g) + 1;
+        uint8_t *const flag_l = lds + L::kOffFlags + c * 4 + q;
+        float *const mq_l = reinterpret_cast<float *>(lds + L::kOffMq) + c * 4 + q;
+        const f32x4 *const mp_l = reinterpret_cast<const f32x4 *>(lds + L::kOffMq) + c;
+        uint8_t *const p_l = lds + L::kOffP + p_off(c, 2 * q + (g >> 1)) + (g & 1) * 8;
         for (int k = 0; k < n_tiles; k++) {
             // row sources of the tile that refills this step's buffer
             const int nx = k + kNB;
             uint64_t nsrc[L::kLoads];
 #pragma unroll
-            for (int i = 0; i < L::kLoads; i++) nsrc[i] = row_src(min(nx, n_tiles - 1), i);
+            for (int i = 0; i < L::kLoads; i++) nsrc[i] = src_l[min(nx, n_tiles - 1) * kTile + 2 * i];
             // QK^T of both head tiles over the quarter's 16 entries
-            f32x4 part[2];
+            f32x4 part[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
             if constexpr (QFP8) {
+                // one chain per head tile through the accumulator input, the
+                // two chains interleaved: the MFMA adds its C input at full
+                // fp32 precision (only its own 128 products are summed with
+                // fewer bits), so the chain equals fp32 sums of the steps
 #pragma unroll
-                for (int nt = 0; nt < 2; nt++) {
-                    f32x4 accg[4];
+                for (int k2 = 0; k2 < 4; k2++) {
+                    const u32x4 &lo = xc[2 * k2], &hi = xc[2 * k2 + 1];
+                    const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 #pragma unroll
-                    for (int k2 = 0; k2 < 4; k2++) {
-                        const u32x4 &lo = xc[2 * k2], &hi = xc[2 * k2 + 1];
-                        const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                        accg[k2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            av, bq8[nt][k2], f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; i++) part[nt][i] = (accg[0][i] + accg[1][i]) + (accg[2][i] + accg[3][i]);
+                    for (int nt = 0; nt < 2; nt++)
+                        part[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            av, bq8[nt][k2], part[nt], 0, 0, 0, 127, 0, 127);
                 }
             } else {
                 // bf16 products of the rows converted FP8 -> bf16 exactly
@@ -1590,45 +1636,44 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
                 for (int nt = 0; nt < 2; nt++) part[nt] = accg[nt][0] + accg[nt][1];
             }
             // softmax of both head tiles (as attn_kernel's owners): entries
-            // 16q + 4g + i of head nt*16 + c
+            // 16q + 4g + i of head nt*16 + c.  A masked entry's row is a zero
+            // row, so its product is exactly 0 and adding -inf masks it.
             const int par = k & 1;
-            const int32_t *slh = reinterpret_cast<const int32_t *>(slots + k * kTile + 16 * q + 4 * g) + 1;
-            const int32_t slv[4] = {slh[0], slh[2], slh[4], slh[6]};
+            float madd[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) madd[i] = mask_term(mask_l[2 * (k * kTile + i)]);
             f32x4 mp[2];
 #pragma unroll
-            for (int nt = 0; nt < 2; nt++)
-                mp[nt] = *reinterpret_cast<const f32x4 *>(lds + L::kOffMq + (par ^ 1) * L::kMqBytes + (nt * 16 + c) * 16);
+            for (int nt = 0; nt < 2; nt++) mp[nt] = mp_l[(par ^ 1) * (L::kMqBytes / 16) + nt * 16];
             // the next tile's row chunks, once this wave's rows of it landed
             // (past the last tile from a stale buffer, unused)
             wait_own(k + 1, k + 3);
             read_xc(k + 1);
-            float *mq_w = reinterpret_cast<float *>(lds + L::kOffMq + par * L::kMqBytes);
-            uint8_t *p_w = lds + L::kOffP + par * L::kPBytes;
+            float sv[2][4], mx[2];
 #pragma unroll
             for (int nt = 0; nt < 2; nt++) {
-                const int hh = nt * 16 + c;
-                float sv[4], mx = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    sv[i] = slv[i] >= 0 ? part[nt][i] * sscale : -INFINITY;
-                    mx = fmaxf(mx, sv[i]);
-                }
-                mx = max_over_g(mx);
+                for (int i = 0; i < 4; i++) sv[nt][i] = __builtin_fmaf(part[nt][i], sscale, madd[i]);
+                mx[nt] = fmaxf(fmaxf(sv[nt][0], sv[nt][1]), fmaxf(sv[nt][2], sv[nt][3]));
+            }
+            max_over_g2(mx[0], mx[1]);
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++) {
                 if (k > 0) {
                     const float r = fmaxf(fmaxf(mp[nt][0], mp[nt][1]), fmaxf(mp[nt][2], mp[nt][3]));
                     m_own[nt] = fmaxf(m_own[nt], r);
                 }
-                const bool moved = mx - m_own[nt] > kSlack;   // false for an all-masked tile
-                if (moved) m_own[nt] = mx;
-                if (g == 0) lds[L::kOffFlags + par * kHB * 4 + hh * 4 + q] = k > 0 && !moved;
+                const bool moved = mx[nt] - m_own[nt] > kSlack;   // false for an all-masked tile
+                if (moved) m_own[nt] = mx[nt];
+                if (g == 0) flag_l[par * kHB * 4 + nt * 64] = k > 0 && !moved;
                 float p[4];
 #pragma unroll
-                for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_own[nt]);
+                for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(sv[nt][i] - m_own[nt]);
                 const f16x2 p01 = {(_Float16)p[0], (_Float16)p[1]};
                 const f16x2 p23 = {(_Float16)p[2], (_Float16)p[3]};
-                *reinterpret_cast<u32x2 *>(p_w + p_off(hh, 2 * q + (g >> 1)) + (g & 1) * 8) =
+                *reinterpret_cast<u32x2 *>(p_l + par * L::kPBytes + nt * 2048) =
                     u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
-                if (g == 0) mq_w[hh * 4 + q] = m_own[nt];
+                if (g == 0) mq_l[par * (L::kMqBytes / 4) + nt * 64] = m_own[nt];
             }
             wait_lgkm0();
             barrier_raw();
@@ -1966,6 +2011,11 @@ static hipError_t launch_nt(const AttnArgs &a, hipStream_t stream) {
 hipError_t launch_attn(const AttnArgs &a_in, int layout, bool q_fp8, bool out_bf16,
                        hipStream_t stream) {
     AttnArgs a = a_in;
+    // masked entries are marked by kMaskBits in their row source: no pool
+    // address may carry any of those bits
+    const uint64_t pool_lo = reinterpret_cast<uint64_t>(a.pool);
+    const uint64_t pool_hi = pool_lo + (uint64_t)a.num_slots * (uint64_t)kBf16RowBytes;
+    if (((pool_lo | pool_hi) & kMaskBits) != 0 || pool_hi < pool_lo) return hipErrorInvalidValue;
     if (a.n_splits < 1) a.n_splits = 1;
     a.split_len = split_len_for(a.K, a.n_splits);
 #define DSA_DISPATCH(L, Q, O) \
