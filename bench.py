@@ -40,6 +40,9 @@ MFMA_BF16_TFLOPS = 2500.0       # dense bf16/f16 matrix peak, published
 MFMA_FP8_TFLOPS = 5000.0        # dense fp8 matrix peak, published
 METRIC = "query tok/s + gathered-KV GB/s (% HBM peak), decode H=16 top-k=2048"
 MIN_TIMING_CALLS = 20           # event-timed attention calls, at least
+# clock cycles of stream spin per bracketed step (about 250 us at 2 GHz, well
+# above the host's cost of enqueueing one step)
+SPIN_CYCLES_PER_STEP = 500_000
 
 
 class TimingEvent:
@@ -258,6 +261,11 @@ def main():
     n_ev = max(MIN_TIMING_CALLS, args.timing_calls)
     events = [tuple(TimingEvent() for _ in range(4)) for _ in range(n_ev)]
     torch.cuda.synchronize()
+    # a spin kernel ahead of the bracketed steps keeps the stream busy while
+    # the host enqueues them, so that every bracket holds GPU time alone
+    # (on an idle stream a start event passes before the host has launched
+    # the kernels it brackets, and the launch cost lands inside)
+    torch.cuda._sleep(n_ev * SPIN_CYCLES_PER_STEP)
     for j in range(n_ev):
         step(first + args.steps + j, events[j])
     torch.cuda.synchronize()
@@ -362,6 +370,7 @@ def bench_transform(args, wl, dev):
     elapsed = time.perf_counter() - t0
     n_ev = max(MIN_TIMING_CALLS, args.timing_calls)
     events = [(TimingEvent(), TimingEvent()) for _ in range(n_ev)]
+    torch.cuda._sleep(n_ev * SPIN_CYCLES_PER_STEP)   # as in the attention timing pass
     for ev in events:
         ev[0].record()
         call()
