@@ -45,6 +45,15 @@ MIN_TIMING_CALLS = 20           # event-timed attention calls, at least
 SPIN_CYCLES_PER_STEP = 500_000
 
 
+def spin(cycles: int) -> None:
+    """A kernel that keeps the current stream busy for about `cycles` clock
+    cycles (PyTorch's own spin kernel; skipped where this build lacks it)."""
+    import torch
+    fn = getattr(torch.cuda, "_sleep", None)
+    if fn is not None:
+        fn(int(cycles))
+
+
 class TimingEvent:
     """A HIP event used only to measure time, recorded on torch's current
     stream (the stream the library launches on).  It is created with
@@ -265,7 +274,7 @@ def main():
     # the host enqueues them, so that every bracket holds GPU time alone
     # (on an idle stream a start event passes before the host has launched
     # the kernels it brackets, and the launch cost lands inside)
-    torch.cuda._sleep(n_ev * SPIN_CYCLES_PER_STEP)
+    spin(n_ev * SPIN_CYCLES_PER_STEP)
     for j in range(n_ev):
         step(first + args.steps + j, events[j])
     torch.cuda.synchronize()
@@ -370,7 +379,7 @@ def bench_transform(args, wl, dev):
     elapsed = time.perf_counter() - t0
     n_ev = max(MIN_TIMING_CALLS, args.timing_calls)
     events = [(TimingEvent(), TimingEvent()) for _ in range(n_ev)]
-    torch.cuda._sleep(n_ev * SPIN_CYCLES_PER_STEP)   # as in the attention timing pass
+    spin(n_ev * SPIN_CYCLES_PER_STEP)   # as in the attention timing pass
     for ev in events:
         ev[0].record()
         call()

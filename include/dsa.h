@@ -99,7 +99,8 @@ typedef enum dsa_status {
     DSA_ERR_WIDTH_MISMATCH = 3, /* latent width is not the 512 of the rows    */
     DSA_ERR_LAYOUT = 4,         /* unknown or unsupported row layout / RoPE   */
     DSA_ERR_DTYPE = 5,          /* unsupported element type (incl. FNUZ)      */
-    DSA_ERR_ALIGN = 6,          /* pointer or stride not 16-byte aligned      */
+    DSA_ERR_ALIGN = 6,          /* pointer or stride not 16-byte aligned (or
+                                   an attention pool reaching 2^55)           */
     DSA_ERR_WORKSPACE = 7,      /* workspace missing or too small             */
     DSA_ERR_DEVICE = 8,         /* current device is not gfx950               */
     DSA_ERR_LAUNCH = 9          /* the HIP runtime refused a launch           */
@@ -190,7 +191,8 @@ size_t dsa_quantize_q_workspace_bytes(int64_t n_elems);
  *   D           must be 512 (DSA_ERR_WIDTH_MISMATCH); rope_dim must be 64
  *               for DSA_KV_SCALED_FP8_656 and 0 otherwise (DSA_ERR_LAYOUT).
  *               1 <= H <= 128.  T == 0 is a no-op.
- *   pool        [num_slots, row bytes of `layout`], 16-byte aligned.
+ *   pool        [num_slots, row bytes of `layout`], 16-byte aligned, below
+ *               address 2^55 (DSA_ERR_ALIGN otherwise; device allocations are).
  *   topk        [T, K] int32; K a positive multiple of 128, at most 65536.
  *               Entry i: -1 is padding; other values are positions resolved
  *               through page_table (or pool slots when page_table is NULL).

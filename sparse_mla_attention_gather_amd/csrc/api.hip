@@ -124,6 +124,11 @@ int32_t validate_attn(const void *q, int32_t q_dtype, const float *q_scale,
     if (!q || !pool || !topk || !out) return DSA_ERR_NULL;
     if (q_dtype == DSA_FP8_E4M3FN && !q_scale) return DSA_ERR_NULL;
     if (!aligned16(q) || !aligned16(pool) || !aligned16(out)) return DSA_ERR_ALIGN;
+    // the kernels mark a masked entry's row source with the bits of -inf in
+    // its high word (0xff800000 << 32): every pool row must lie below 2^55
+    const uint64_t pool_end = reinterpret_cast<uint64_t>(pool) +
+                              static_cast<uint64_t>(num_slots) * static_cast<uint64_t>(dsa_kv_row_bytes(layout));
+    if ((pool_end >> 55) != 0 || pool_end < reinterpret_cast<uint64_t>(pool)) return DSA_ERR_ALIGN;
     const size_t need = dsa::attn_workspace_bytes(T, H, K, phase, split_target_cus());
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
