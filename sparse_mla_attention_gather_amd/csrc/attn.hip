@@ -200,6 +200,15 @@ __device__ __forceinline__ float max_over_g(float v) {
     const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// Two fp32 values as packed bf16 (low half first), rounded to nearest even
+// by gfx950's v_cvt_pk_bf16_f32: bit for bit the rounding of
+// f32_to_bf16_bits (a device probe compared them over every exponent and
+// sign with ties and near-ties in the low half), NaN staying NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 // The maxima over g of two values at once: the first swap pairs the lanes
 // l, l ^ 32 of a in lanes 0-31 and those of b in lanes 32-63, the second the
 // 16-lane rows, the third hands every lane both results.
@@ -923,13 +932,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         // rounded.  (32-head blocks: attn_w8_kernel, one f16 term.)
         const int poff = p_off(hh, 2 * wq + (g >> 1)) + (g & 1) * 8;
         if constexpr (LAYOUT == 3) {
-            uint32_t b[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                b[i] = f32_to_bf16_bits(p[i]);
-                l_part += bf16_bits_to_f32(b[i]);
-            }
-            *reinterpret_cast<u32x2 *>(p_w + poff) = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+            const uint32_t b01 = pack_bf16x2(p[0], p[1]), b23 = pack_bf16x2(p[2], p[3]);
+            l_part += bf16_bits_to_f32(b01 & 0xffffu);
+            l_part += bf16_bits_to_f32(b01 >> 16);
+            l_part += bf16_bits_to_f32(b23 & 0xffffu);
+            l_part += bf16_bits_to_f32(b23 >> 16);
+            *reinterpret_cast<u32x2 *>(p_w + poff) = u32x2{b01, b23};
         } else {
             const f16x2 p01 = {(_Float16)p[0], (_Float16)p[1]};
             const f16x2 p23 = {(_Float16)p[2], (_Float16)p[3]};
@@ -1084,7 +1092,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                         for (int e = 0; e < 4; e++) {
                             const float lo = bf16_bits_to_f32(b[e] & 0xffffu) * fq[nt][ks];
                             const float hi = bf16_bits_to_f32(b[e] >> 16) * fq[nt][ks];
-                            b[e] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+                            b[e] = pack_bf16x2(lo, hi);
                         }
                         bp[nt][ks] = __builtin_bit_cast(f16x8, b);
                     } else if constexpr (L::kLo) {
@@ -1201,8 +1209,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 for (int dt = 0; dt < kDT; dt++) {
                     const f32x4 o = acc[dt][nt] * inv;
                     if (OUT_BF16) {
-                        u32x2 pk = {f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
-                                    f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16)};
+                        u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
                         *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + base + dt * 16) = pk;
                     } else {
                         *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + base + dt * 16) = o;
@@ -1822,8 +1829,7 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
             for (int dt = 0; dt < kDT; dt++) {
                 const f32x4 o = acc[dt][nt] * inv;
                 if (OUT_BF16) {
-                    u32x2 pk = {f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
-                                f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16)};
+                    u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
                     *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + base + dt * 16) = pk;
                 } else {
                     *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + base + dt * 16) = o;
@@ -1886,10 +1892,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     o0 *= inv;
     o1 *= inv;
     if (OUT_BF16) {
-        u32x4 pk = {f32_to_bf16_bits(o0[0]) | (f32_to_bf16_bits(o0[1]) << 16),
-                    f32_to_bf16_bits(o0[2]) | (f32_to_bf16_bits(o0[3]) << 16),
-                    f32_to_bf16_bits(o1[0]) | (f32_to_bf16_bits(o1[1]) << 16),
-                    f32_to_bf16_bits(o1[2]) | (f32_to_bf16_bits(o1[3]) << 16)};
+        u32x4 pk = {pack_bf16x2(o0[0], o0[1]), pack_bf16x2(o0[2], o0[3]),
+                    pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3])};
         *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(a.out) + th * kD + lane * 8) = pk;
     } else {
         float *dst = reinterpret_cast<float *>(a.out) + th * kD + lane * 8;
