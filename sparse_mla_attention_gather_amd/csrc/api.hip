@@ -179,6 +179,10 @@ int32_t run_attn(int32_t phase, const void *q, int32_t q_dtype,
     a.n_splits = dsa::attn_splits(T, H, K, phase, layout, split_target_cus());
     a.split_len = 0;
     a.err_count = err_count;
+    // prefill: one 32-head workgroup per compute unit (a multiple of 8, so
+    // that a workgroup's units keep their XCD), each taking its share of
+    // the units with the next unit's entries resolved ahead
+    a.grid_cap = phase == 1 ? std::max(8, split_target_cus() / 8 * 8) : 0;
     hipError_t e = dsa::launch_attn(a, layout, q_dtype == DSA_FP8_E4M3FN,
                                     out_dtype == DSA_BF16,
                                     static_cast<hipStream_t>(stream));

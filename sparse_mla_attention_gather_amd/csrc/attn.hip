@@ -1370,7 +1370,8 @@ struct W8 {
     static constexpr int kMqBytes = kHB * 16;
     static constexpr int kOffRedL = kOffMq + 2 * kMqBytes;     // last entries, then denominators
     static constexpr int kOffFlags = kOffRedL + kHB * 16;      // [32][4] bytes, two
-    static constexpr int kBytes = kOffFlags + 2 * kHB * 4;
+    static constexpr int kOffLast = kOffFlags + 2 * kHB * 4;   // a unit's last valid entries [8]
+    static constexpr int kBytes = kOffLast + 8 * 4;
     static constexpr int kDT = 8;                              // PV: 16-dim tiles per wave
     static constexpr int kLoads = 8;                           // DMA instructions per scoring wave and tile
     // the page-table row is staged in tile buffer 2 (free until after the prologue)
@@ -1393,29 +1394,44 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
     const int dbase = 128 * (w - 4);             // PV: first of this wave's dims
     const int n_hb = (a.H + kHB - 1) / kHB;
 
-    // XCD-aware numbering, as in attn_kernel
+    // Units in XCD-aware numbering, as in attn_kernel: virtual block v is
+    // token (v >> 3) / per_tok * 8 + (v & 7), head block and split.  A
+    // workgroup takes the virtual blocks blockIdx.x, + gridDim.x, ... (the
+    // Q8 prefill launches one workgroup per compute unit, gridDim.x a
+    // multiple of 8, so that a workgroup's units keep its XCD); from its
+    // second unit on, a unit's entries were resolved into LDS at the end of
+    // the previous one (resolve_next), so that its start needs no prologue.
     const int per_tok = n_hb * a.n_splits;
-    const int x = blockIdx.x & 7;
-    const int kq = blockIdx.x >> 3;
-    const int t = (kq / per_tok) * 8 + x;
-    if (t >= a.T) return;
-    const int hb = (kq % per_tok) / a.n_splits;
-    const int split = kq % a.n_splits;
+    const int n_virt = (a.T + 7) / 8 * 8 * per_tok;
+    int t = 0, hb = 0, split = 0, begin = 0, n_ent = 0;   // the current unit
+    auto set_unit = [&](int v) {
+        const int kqv = v >> 3;
+        t = (kqv / per_tok) * 8 + (v & 7);
+        hb = (kqv % per_tok) / a.n_splits;
+        split = kqv % a.n_splits;
+        begin = split * a.split_len;
+        n_ent = min(a.K - begin, a.split_len);   // a multiple of 64
+        return v < n_virt && t < a.T;            // (past the last token, so is every later one)
+    };
+    if (!set_unit(blockIdx.x)) return;
+    // (several units per workgroup with an FP8 query only: with a bf16 query
+    // the scoring waves' registers leave no room for the unit loop)
+    constexpr bool kPersist = QFP8;
 
     uint64_t *slots = reinterpret_cast<uint64_t *>(lds + L::kOffSlots);   // row sources
     float *rl_lds = reinterpret_cast<float *>(lds + L::kOffRedL);
-    const int seq = a.token_seq ? a.token_seq[t] : t;
-    const bool seq_ok = (a.page_table == nullptr && a.seq_lens == nullptr) ||
-                        (seq >= 0 && seq < a.num_seqs);
-    const int seq_len = (a.seq_lens && seq_ok) ? a.seq_lens[seq] : INT_MAX;
-    const int begin = split * a.split_len;
-    const int n_ent = min(a.K - begin, a.split_len);   // a multiple of 64
+    int *last_lds = reinterpret_cast<int *>(lds + L::kOffLast);
     const float sscale = a.softmax_scale * kLog2e * (QFP8 ? *a.q_scale : 1.0f);
 
-    // ---- prologue: the split's entries resolved to row sources in LDS (as
+    // ---- prologue of the workgroup's first unit: its entries resolved to
+    // row sources in LDS (as
     // in attn_kernel: unconditional loads, the page-table row staged when it
     // fits, the last valid entry found by ballots)
     {
+        const int seq = a.token_seq ? a.token_seq[t] : t;
+        const bool seq_ok = (a.page_table == nullptr && a.seq_lens == nullptr) ||
+                            (seq >= 0 && seq < a.num_seqs);
+        const int seq_len = (a.seq_lens && seq_ok) ? a.seq_lens[seq] : INT_MAX;
         constexpr int kPer = kMaxSplit / L::kThreads;
         constexpr int kPtCap = L::kPtPer * L::kThreads;
         const int32_t *tk = a.topk + (int64_t)t * a.K + begin;
@@ -1471,18 +1487,18 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
             const uint64_t vb = __builtin_amdgcn_ballot_w64(j < n_ent && s >= 0);
             if (vb) last = max(last, w * 64 + 63 - (int)__builtin_clzll(vb) + i * L::kThreads);
         }
-        if (lane == 0) reinterpret_cast<int *>(rl_lds)[w] = last;
+        if (lane == 0) last_lds[w] = last;
         if (a.err_count && hb == 0 && lane == 0 && n_err) atomicAdd(a.err_count, n_err);
     }
     __syncthreads();
     const uint32_t lds0 = lds_addr(lds);
-    int n_tiles;
-    {
-        const int4 *lw = reinterpret_cast<const int4 *>(rl_lds);
+    int n_tiles = 1;
+    auto read_n_tiles = [&] {
+        const int4 *lw = reinterpret_cast<const int4 *>(last_lds);
         const int4 v0 = lw[0], v1 = lw[1];
         const int last = max(max(max(v0.x, v0.y), max(v0.z, v0.w)), max(max(v1.x, v1.y), max(v1.z, v1.w)));
         n_tiles = __builtin_amdgcn_readfirstlane(max(1, (last + kTile) / kTile));
-    }
+    };
 
     // ---- scoring waves: the tile DMA of their quarter's rows (two rows per
     // instruction: lane l -> row 16q + 2k + (l >> 5), position l & 31
@@ -1518,326 +1534,434 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
     // tiles, so that the wait for tile 0 covers it
     uint8_t *const qst = lds + 3 * L::kBufBytes;
     static_assert(kHB * kQRowBytes <= L::kBufBytes, "query copy fits a tile buffer");
-    auto q_global = [&](int hl, int byte) {
-        const int h = hb * kHB + hl;
-        return reinterpret_cast<const uint8_t *>(a.q) + ((int64_t)t * a.H + (h < a.H ? h : 0)) * kQRowBytes + byte;
+    auto q_global = [&](int tq, int hbq, int hl, int byte) {
+        const int h = hbq * kHB + hl;
+        return reinterpret_cast<const uint8_t *>(a.q) + ((int64_t)tq * a.H + (h < a.H ? h : 0)) * kQRowBytes + byte;
+    };
+    // this scoring wave's share of the query copy of (token tq, head block hbq)
+    auto issue_q = [&](int tq, int hbq) {
+        constexpr int kPerWave = kHB * kQChunks / 4;   // chunks copied by each scoring wave
+        const uint32_t qbase = lds_addr(qst);
+#pragma unroll
+        for (int i0 = 0; i0 < kPerWave; i0 += 64) {
+            const int i = q * kPerWave + i0 + lane;
+            const int hl = i / kQChunks, kp = i % kQChunks;
+            dma16(q_global(tq, hbq, hl, (kp ^ (hl & 7)) << 4), qbase + (q * kPerWave + i0) * 16);
+        }
     };
     auto q_lds = [&](int hl, int chunk) {
         return reinterpret_cast<const u32x4 *>(qst + hl * kQRowBytes + ((chunk ^ (hl & 7)) << 4));
     };
 
+    // The next unit (virtual block vn), started by the scoring waves while
+    // the PV waves run the unit's last tile and write its output: its top-k
+    // words and token are loaded during the last scoring step
+    // (fetch_next), its page-table words, resolution and slot array follow
+    // the loop (start_next), and each scoring wave then issues its share of
+    // the next query copy and its rows of the next unit's first three tiles.
+    // After the last step no wave reads a tile buffer or the slot array any
+    // more, so all four buffers are free.  Lane (c, g) of wave q resolves
+    // entries (4 i + g) * 64 + 16 q + c (i < 8): the rows that wave q copies
+    // in every tile, so that its copies read only slots it wrote itself.
+    constexpr int kPf = kMaxSplit / (4 * kTile);
+    auto next_coords = [&](int vn, int &tn, int &hbn, int &begin_n, int &n_ent_n) {
+        const int kqn = vn >> 3;
+        tn = (kqn / per_tok) * 8 + (vn & 7);
+        hbn = (kqn % per_tok) / a.n_splits;
+        begin_n = (kqn % a.n_splits) * a.split_len;
+        n_ent_n = min(a.K - begin_n, a.split_len);
+        return vn < n_virt && tn < a.T;
+    };
+    auto fetch_next = [&](int vn, int32_t (&v)[kPf], int32_t &seq_v) {
+        int tn, hbn, begin_n, n_ent_n;
+        next_coords(vn, tn, hbn, begin_n, n_ent_n);
+        const int32_t *tk = a.topk + (int64_t)tn * a.K + begin_n;
+#pragma unroll
+        for (int i = 0; i < kPf; i++) {
+            const int e = (4 * i + g) * kTile + 16 * q + c;
+            const int32_t xv = tk[min(e, n_ent_n - 1)];
+            v[i] = e < n_ent_n ? xv : -1;
+        }
+        // a vector load (the token is uniform): the step's LDS waits then do
+        // not wait for it
+        int tsel = tn;
+        asm volatile("" : "+v"(tsel));
+        seq_v = a.token_seq ? a.token_seq[tsel] : tsel;
+    };
+    auto start_next = [&](int vn, const int32_t (&v)[kPf], int32_t seq_v) {
+        int tn, hbn, begin_n, n_ent_n;
+        next_coords(vn, tn, hbn, begin_n, n_ent_n);
+        const int sq = __builtin_amdgcn_readfirstlane(seq_v);
+        const bool sq_ok = (a.page_table == nullptr && a.seq_lens == nullptr) || (sq >= 0 && sq < a.num_seqs);
+        const int32_t *row = a.page_table + (int64_t)(sq_ok ? sq : 0) * a.max_pages;
+        int32_t phys[kPf];
+        int ssel = sq_ok ? sq : 0;
+        asm volatile("" : "+v"(ssel));
+        const int sq_len_v = (a.seq_lens && sq_ok) ? a.seq_lens[ssel] : INT_MAX;
+#pragma unroll
+        for (int i = 0; i < kPf; i++)
+            phys[i] = a.page_table ? row[min(max(v[i], 0) >> a.page_shift, a.max_pages - 1)] : 0;
+        const int sq_len = sq_ok ? __builtin_amdgcn_readfirstlane(sq_len_v) : INT_MAX;
+        int n_err = 0, last = -1;
+#pragma unroll
+        for (int i = 0; i < kPf; i++) {
+            const int e = (4 * i + g) * kTile + 16 * q + c;
+            bool err;
+            const int32_t s = resolve_entry(a, v[i], phys[i], sq_ok, sq_len, err);
+            n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(err));
+            if (e < n_ent_n)
+                slots[e] = s >= 0 ? reinterpret_cast<uint64_t>(a.pool + (int64_t)s * kRawBytes)
+                                  : reinterpret_cast<uint64_t>(kZeroRow + (16 * q + c) * kRawBytes) | kMaskBits;
+            // the highest tile of step i holding a valid entry
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(e < n_ent_n && s >= 0);
+            if (bal) last = (4 * i + ((63 - (int)__builtin_clzll(bal)) >> 4)) * kTile;
+        }
+        if (lane == 0) {
+            last_lds[w] = last;
+            last_lds[w + 4] = -1;
+        }
+        if (a.err_count && hbn == 0 && lane == 0 && n_err) atomicAdd(a.err_count, n_err);
+        // (the copies below read this wave's own slot stores, in order)
+        asm volatile("" ::: "memory");
+        issue_q(tn, hbn);
+#pragma unroll
+        for (int j = 0; j < 3; j++)
+            if (j * kTile < n_ent_n) issue_tile8(j);
+    };
+
     if (__builtin_amdgcn_readfirstlane((int)is_v) == 0) {
         // ================= scoring waves =================
-        {
-            constexpr int kPerWave = kHB * kQChunks / 4;   // chunks copied by each scoring wave
-            const uint32_t qbase = lds_addr(qst);
-#pragma unroll
-            for (int i0 = 0; i0 < kPerWave; i0 += 64) {
-                const int i = q * kPerWave + i0 + lane;
-                const int hl = i / kQChunks, kp = i % kQChunks;
-                dma16(q_global(hl, (kp ^ (hl & 7)) << 4), qbase + (q * kPerWave + i0) * 16);
+        // (from the second unit on, the query copy and tiles 0-2 were issued
+        // at the end of the previous one)
+        for (int vb = blockIdx.x, pref = 0;; pref = 1) {
+            read_n_tiles();
+            if (!pref) {
+                issue_q(t, hb);
+                issue_tile8(0);
+                if (n_tiles > 1) issue_tile8(1);
             }
-        }
-        issue_tile8(0);
-        if (n_tiles > 1) issue_tile8(1);
-        wait_own(0, 1);
-        barrier_raw();                       // tile 0 and the query copy landed
-        // The query of both head tiles as the B operand.  FP8:
-        // bq8[nt][k2] = q8[h][128 k2 + 32 g .. +32] (chunks 8 k2 + 2g, +1);
-        // bf16: bq[nt][kk] = q[h][d .. d+8] with d = (4 (kk >> 1) + g) * 16 +
-        // 8 (kk & 1), so that a lane's steps 2m, 2m+1 use the two halves of
-        // one 16-byte row chunk (the reduction index is free: A and B agree).
-        i32x8 bq8[QFP8 ? 2 : 1][QFP8 ? 4 : 1];
-        bf16x8 bq[QFP8 ? 1 : 2][QFP8 ? 1 : 16];
-#pragma unroll
-        for (int nt = 0; nt < 2; nt++) {
-            const int hl = nt * 16 + c;
-            if constexpr (QFP8) {
-#pragma unroll
-                for (int k2 = 0; k2 < 4; k2++) {
-                    const u32x4 lo = *q_lds(hl, 8 * k2 + 2 * g), hi = *q_lds(hl, 8 * k2 + 2 * g + 1);
-                    bq8[nt][k2] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                }
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < 16; kk++)
-                    // (bf16 row bytes: chunk 2 d / 16)
-                    bq[nt][kk] = __builtin_bit_cast(bf16x8, *q_lds(hl, ((4 * (kk >> 1) + g) * 16 + 8 * (kk & 1)) / 8));
-            }
-        }
-        // row chunks of the quarter's row 16q + c: FP8 step k2 takes chunks
-        // 8 k2 + 2g and 8 k2 + 2g + 1, bf16 steps 2m, 2m+1 the halves of
-        // chunk 4m + g
-        u32x4 xc[8];
-        auto read_xc = [&](int j) {
-            const int r = 16 * q + c;
-            const uint8_t *xr = lds + (j % kNB) * L::kBufBytes + r * kRawBytes;
-            const int sw = swz<0>(r);
-            // chunk ch(m + 4) = ch(m) + 16, and the swizzle (< 16) leaves bit
-            // 4 of a chunk index alone: steps m and m + 4 share an address,
-            // 256 bytes apart
-#pragma unroll
-            for (int m = 0; m < 4; m++) {
-                const int ch = QFP8 ? (m >> 1) * 8 + g * 2 + (m & 1) : 4 * m + g;
-                const uint8_t *xa = xr + ((ch ^ sw) * 16);
-                xc[m] = *reinterpret_cast<const u32x4 *>(xa);
-                xc[m + 4] = *reinterpret_cast<const u32x4 *>(xa + 256);
-            }
-        };
-        read_xc(0);
-        if (n_tiles > 2) issue_tile8(2);
-        wait_lgkm0();
-        barrier_raw();                       // every scoring wave holds the query
-        if (n_tiles > 3) issue_tile8(3);
-
-        float m_own[2] = {kNoMax, kNoMax};
-        // this lane's LDS addresses in the step, less their per-tile parts
-        // (head tile nt adds 16 heads: 64 bytes of flags and maxima, 2 KB of
-        // P, since the P swizzle (hh >> 1) & 7 does not see nt)
-        const uint64_t *const src_l = slots + 16 * q + (lane >> 5);          // + j kTile + 2 i
-        const int32_t *const mask_l = reinterpret_cast<const int32_t *>(slots + 16 * q + 4 * g) + 1;
-        uint8_t *const flag_l = lds + L::kOffFlags + c * 4 + q;
-        float *const mq_l = reinterpret_cast<float *>(lds + L::kOffMq) + c * 4 + q;
-        const f32x4 *const mp_l = reinterpret_cast<const f32x4 *>(lds + L::kOffMq) + c;
-        uint8_t *const p_l = lds + L::kOffP + p_off(c, 2 * q + (g >> 1)) + (g & 1) * 8;
-        for (int k = 0; k < n_tiles; k++) {
-            // row sources of the tile that refills this step's buffer
-            const int nx = k + kNB;
-            uint64_t nsrc[L::kLoads];
-#pragma unroll
-            for (int i = 0; i < L::kLoads; i++) nsrc[i] = src_l[min(nx, n_tiles - 1) * kTile + 2 * i];
-            // QK^T of both head tiles over the quarter's 16 entries
-            f32x4 part[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
-            if constexpr (QFP8) {
-                // one chain per head tile through the accumulator input, the
-                // two chains interleaved: the MFMA adds its C input at full
-                // fp32 precision (only its own 128 products are summed with
-                // fewer bits), so the chain equals fp32 sums of the steps
-#pragma unroll
-                for (int k2 = 0; k2 < 4; k2++) {
-                    const u32x4 &lo = xc[2 * k2], &hi = xc[2 * k2 + 1];
-                    const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-#pragma unroll
-                    for (int nt = 0; nt < 2; nt++)
-                        part[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            av, bq8[nt][k2], part[nt], 0, 0, 0, 127, 0, 127);
-                }
-            } else {
-                // bf16 products of the rows converted FP8 -> bf16 exactly
-                // (each converted operand feeds both head tiles), fp32 sums
-                // in two chains per head tile
-                f32x4 accg[2][2];
-#pragma unroll
-                for (int nt = 0; nt < 2; nt++) accg[nt][0] = accg[nt][1] = f32x4{0, 0, 0, 0};
-#pragma unroll
-                for (int kk = 0; kk < 16; kk++) {
-                    const u32x4 &ch = xc[kk >> 1];
-                    const bf16x8 av = (kk & 1) ? e4m3x8_to_bf16(ch[2], ch[3]) : e4m3x8_to_bf16(ch[0], ch[1]);
-#pragma unroll
-                    for (int nt = 0; nt < 2; nt++)
-                        accg[nt][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[nt][kk], accg[nt][kk & 1], 0, 0, 0);
-                }
-#pragma unroll
-                for (int nt = 0; nt < 2; nt++) part[nt] = accg[nt][0] + accg[nt][1];
-            }
-            // softmax of both head tiles (as attn_kernel's owners): entries
-            // 16q + 4g + i of head nt*16 + c.  A masked entry's row is a zero
-            // row, so its product is exactly 0 and adding -inf masks it.
-            const int par = k & 1;
-            float madd[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) madd[i] = mask_term(mask_l[2 * (k * kTile + i)]);
-            f32x4 mp[2];
-#pragma unroll
-            for (int nt = 0; nt < 2; nt++) mp[nt] = mp_l[(par ^ 1) * (L::kMqBytes / 16) + nt * 16];
-            // the next tile's row chunks, once this wave's rows of it landed
-            // (past the last tile from a stale buffer, unused)
-            wait_own(k + 1, k + 3);
-            read_xc(k + 1);
-            float sv[2][4], mx[2];
+            wait_own(0, pref ? 2 : 1);
+            barrier_raw();                       // tile 0 and the query copy landed
+            // The query of both head tiles as the B operand.  FP8:
+            // bq8[nt][k2] = q8[h][128 k2 + 32 g .. +32] (chunks 8 k2 + 2g, +1);
+            // bf16: bq[nt][kk] = q[h][d .. d+8] with d = (4 (kk >> 1) + g) * 16 +
+            // 8 (kk & 1), so that a lane's steps 2m, 2m+1 use the two halves of
+            // one 16-byte row chunk (the reduction index is free: A and B agree).
+            i32x8 bq8[QFP8 ? 2 : 1][QFP8 ? 4 : 1];
+            bf16x8 bq[QFP8 ? 1 : 2][QFP8 ? 1 : 16];
 #pragma unroll
             for (int nt = 0; nt < 2; nt++) {
+                const int hl = nt * 16 + c;
+                if constexpr (QFP8) {
 #pragma unroll
-                for (int i = 0; i < 4; i++) sv[nt][i] = __builtin_fmaf(part[nt][i], sscale, madd[i]);
-                mx[nt] = fmaxf(fmaxf(sv[nt][0], sv[nt][1]), fmaxf(sv[nt][2], sv[nt][3]));
-            }
-            max_over_g2(mx[0], mx[1]);
+                    for (int k2 = 0; k2 < 4; k2++) {
+                        const u32x4 lo = *q_lds(hl, 8 * k2 + 2 * g), hi = *q_lds(hl, 8 * k2 + 2 * g + 1);
+                        bq8[nt][k2] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    }
+                } else {
 #pragma unroll
-            for (int nt = 0; nt < 2; nt++) {
-                if (k > 0) {
-                    const float r = fmaxf(fmaxf(mp[nt][0], mp[nt][1]), fmaxf(mp[nt][2], mp[nt][3]));
-                    m_own[nt] = fmaxf(m_own[nt], r);
+                    for (int kk = 0; kk < 16; kk++)
+                        // (bf16 row bytes: chunk 2 d / 16)
+                        bq[nt][kk] = __builtin_bit_cast(bf16x8, *q_lds(hl, ((4 * (kk >> 1) + g) * 16 + 8 * (kk & 1)) / 8));
                 }
-                const bool moved = mx[nt] - m_own[nt] > kSlack;   // false for an all-masked tile
-                if (moved) m_own[nt] = mx[nt];
-                if (g == 0) flag_l[par * kHB * 4 + nt * 64] = k > 0 && !moved;
-                float p[4];
-#pragma unroll
-                for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(sv[nt][i] - m_own[nt]);
-                const f16x2 p01 = {(_Float16)p[0], (_Float16)p[1]};
-                const f16x2 p23 = {(_Float16)p[2], (_Float16)p[3]};
-                *reinterpret_cast<u32x2 *>(p_l + par * L::kPBytes + nt * 2048) =
-                    u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
-                if (g == 0) mq_l[par * (L::kMqBytes / 4) + nt * 64] = m_own[nt];
             }
+            // row chunks of the quarter's row 16q + c: FP8 step k2 takes chunks
+            // 8 k2 + 2g and 8 k2 + 2g + 1, bf16 steps 2m, 2m+1 the halves of
+            // chunk 4m + g
+            u32x4 xc[8];
+            auto read_xc = [&](int j) {
+                const int r = 16 * q + c;
+                const uint8_t *xr = lds + (j % kNB) * L::kBufBytes + r * kRawBytes;
+                const int sw = swz<0>(r);
+                // chunk ch(m + 4) = ch(m) + 16, and the swizzle (< 16) leaves bit
+                // 4 of a chunk index alone: steps m and m + 4 share an address,
+                // 256 bytes apart
+#pragma unroll
+                for (int m = 0; m < 4; m++) {
+                    const int ch = QFP8 ? (m >> 1) * 8 + g * 2 + (m & 1) : 4 * m + g;
+                    const uint8_t *xa = xr + ((ch ^ sw) * 16);
+                    xc[m] = *reinterpret_cast<const u32x4 *>(xa);
+                    xc[m + 4] = *reinterpret_cast<const u32x4 *>(xa + 256);
+                }
+            };
+            read_xc(0);
+            if (!pref && n_tiles > 2) issue_tile8(2);
             wait_lgkm0();
-            barrier_raw();
-            if (nx < n_tiles) issue(nx, nsrc);
+            barrier_raw();                       // every scoring wave holds the query
+            if (n_tiles > 3) issue_tile8(3);
+
+            float m_own[2] = {kNoMax, kNoMax};
+            // this lane's LDS addresses in the step, less their per-tile parts
+            // (head tile nt adds 16 heads: 64 bytes of flags and maxima, 2 KB of
+            // P, since the P swizzle (hh >> 1) & 7 does not see nt)
+            const uint64_t *const src_l = slots + 16 * q + (lane >> 5);          // + j kTile + 2 i
+            const int32_t *const mask_l = reinterpret_cast<const int32_t *>(slots + 16 * q + 4 * g) + 1;
+            uint8_t *const flag_l = lds + L::kOffFlags + c * 4 + q;
+            float *const mq_l = reinterpret_cast<float *>(lds + L::kOffMq) + c * 4 + q;
+            const f32x4 *const mp_l = reinterpret_cast<const f32x4 *>(lds + L::kOffMq) + c;
+            uint8_t *const p_l = lds + L::kOffP + p_off(c, 2 * q + (g >> 1)) + (g & 1) * 8;
+            const int vn = vb + (int)gridDim.x;
+            bool has_next = false;
+            if (kPersist) {
+                int tn, hbn, begin_n, n_ent_n;
+                has_next = next_coords(vn, tn, hbn, begin_n, n_ent_n);
+            }
+            int32_t nwords[kPf], nseq = 0;
+            // one step: the last one apart (last_step), so that the next
+            // unit's words are live only from there on
+            auto step = [&](const int k, const bool last_step) {
+                if (last_step && has_next) fetch_next(vn, nwords, nseq);
+                // row sources of the tile that refills this step's buffer
+                const int nx = k + kNB;
+                uint64_t nsrc[L::kLoads];
+#pragma unroll
+                for (int i = 0; i < L::kLoads; i++) nsrc[i] = src_l[min(nx, n_tiles - 1) * kTile + 2 * i];
+                // QK^T of both head tiles over the quarter's 16 entries
+                f32x4 part[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+                if constexpr (QFP8) {
+                    // one chain per head tile through the accumulator input, the
+                    // two chains interleaved: the MFMA adds its C input at full
+                    // fp32 precision (only its own 128 products are summed with
+                    // fewer bits), so the chain equals fp32 sums of the steps
+#pragma unroll
+                    for (int k2 = 0; k2 < 4; k2++) {
+                        const u32x4 &lo = xc[2 * k2], &hi = xc[2 * k2 + 1];
+                        const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+                        for (int nt = 0; nt < 2; nt++)
+                            part[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                av, bq8[nt][k2], part[nt], 0, 0, 0, 127, 0, 127);
+                    }
+                } else {
+                    // bf16 products of the rows converted FP8 -> bf16 exactly
+                    // (each converted operand feeds both head tiles), fp32 sums
+                    // in two chains per head tile
+                    f32x4 accg[2][2];
+#pragma unroll
+                    for (int nt = 0; nt < 2; nt++) accg[nt][0] = accg[nt][1] = f32x4{0, 0, 0, 0};
+#pragma unroll
+                    for (int kk = 0; kk < 16; kk++) {
+                        const u32x4 &ch = xc[kk >> 1];
+                        const bf16x8 av = (kk & 1) ? e4m3x8_to_bf16(ch[2], ch[3]) : e4m3x8_to_bf16(ch[0], ch[1]);
+#pragma unroll
+                        for (int nt = 0; nt < 2; nt++)
+                            accg[nt][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[nt][kk], accg[nt][kk & 1], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int nt = 0; nt < 2; nt++) part[nt] = accg[nt][0] + accg[nt][1];
+                }
+                // softmax of both head tiles (as attn_kernel's owners): entries
+                // 16q + 4g + i of head nt*16 + c.  A masked entry's row is a zero
+                // row, so its product is exactly 0 and adding -inf masks it.
+                const int par = k & 1;
+                float madd[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) madd[i] = mask_term(mask_l[2 * (k * kTile + i)]);
+                f32x4 mp[2];
+#pragma unroll
+                for (int nt = 0; nt < 2; nt++) mp[nt] = mp_l[(par ^ 1) * (L::kMqBytes / 16) + nt * 16];
+                // the next tile's row chunks, once this wave's rows of it landed
+                // (none after the last: every copy has landed then)
+                if (!last_step) {
+                    wait_own(k + 1, k + 3);
+                    read_xc(k + 1);
+                }
+                float sv[2][4], mx[2];
+#pragma unroll
+                for (int nt = 0; nt < 2; nt++) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) sv[nt][i] = __builtin_fmaf(part[nt][i], sscale, madd[i]);
+                    mx[nt] = fmaxf(fmaxf(sv[nt][0], sv[nt][1]), fmaxf(sv[nt][2], sv[nt][3]));
+                }
+                max_over_g2(mx[0], mx[1]);
+#pragma unroll
+                for (int nt = 0; nt < 2; nt++) {
+                    if (k > 0) {
+                        const float r = fmaxf(fmaxf(mp[nt][0], mp[nt][1]), fmaxf(mp[nt][2], mp[nt][3]));
+                        m_own[nt] = fmaxf(m_own[nt], r);
+                    }
+                    const bool moved = mx[nt] - m_own[nt] > kSlack;   // false for an all-masked tile
+                    if (moved) m_own[nt] = mx[nt];
+                    if (g == 0) flag_l[par * kHB * 4 + nt * 64] = k > 0 && !moved;
+                    float p[4];
+#pragma unroll
+                    for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(sv[nt][i] - m_own[nt]);
+                    const f16x2 p01 = {(_Float16)p[0], (_Float16)p[1]};
+                    const f16x2 p23 = {(_Float16)p[2], (_Float16)p[3]};
+                    *reinterpret_cast<u32x2 *>(p_l + par * L::kPBytes + nt * 2048) =
+                        u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+                    if (g == 0) mq_l[par * (L::kMqBytes / 4) + nt * 64] = m_own[nt];
+                }
+                wait_lgkm0();
+                barrier_raw();
+                if (!last_step && nx < n_tiles) issue(nx, nsrc);
+            };
+            for (int k = 0; k < n_tiles - 1; k++) step(k, false);
+            step(n_tiles - 1, true);
+            if (has_next) start_next(vn, nwords, nseq);
+            __syncthreads();                 // the PV waves' epilogue barrier
+            vb = vn;
+            if (!kPersist || !set_unit(vb)) break;
         }
-        __syncthreads();                     // the PV waves' epilogue barrier
         return;
     }
 
     // ================= PV waves =================
-    f32x4 acc[kDT][2], lacc[2];
-    float m_ref[2] = {kNoMax, kNoMax};
+    for (int vb = blockIdx.x;;) {
+        read_n_tiles();
+        f32x4 acc[kDT][2], lacc[2];
+        float m_ref[2] = {kNoMax, kNoMax};
 #pragma unroll
-    for (int nt = 0; nt < 2; nt++) {
-        lacc[nt] = f32x4{0, 0, 0, 0};
+        for (int nt = 0; nt < 2; nt++) {
+            lacc[nt] = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int dt = 0; dt < kDT; dt++) acc[dt][nt] = f32x4{0, 0, 0, 0};
-    }
-    // transpose operands of a tile: lane (c, g) addresses entry
-    // ks*32 + g*8 + (c >> 1), half (c & 1) of the chunk of dims dbase + 16 dt
-    u32x2 tv[2][kDT];
-    auto read_tv = [&](int j) {
-        const uint8_t *xb = lds + (j % kNB) * L::kBufBytes;
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-            const int row = ks * 32 + g * 8 + (c >> 1);
-            const uint8_t *rp = xb + row * kRawBytes + (c & 1) * 8;
-            const int sw = swz<0>(row);
-#pragma unroll
-            for (int dt = 0; dt < kDT; dt++)
-                tv[ks][dt] = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_i32x2 *>(
-                               LDS_PTR(rp + (((dbase / 16 + dt) ^ sw) * 16)))));
+            for (int dt = 0; dt < kDT; dt++) acc[dt][nt] = f32x4{0, 0, 0, 0};
         }
-    };
-    // P of tile j (weighted by 2^(m_q - m_ref) while a quarter's maximum
-    // differs from the reference, O rescaled when the reference moves), the
-    // denominator from the operand (wave 4), then the product over the
-    // wave's dims
-    auto pv = [&](int j) {
-        const int ppar = j & 1;
-        const float *mq_lds = reinterpret_cast<const float *>(lds + L::kOffMq + ppar * L::kMqBytes);
-        const uint8_t *p_lds = lds + L::kOffP + ppar * L::kPBytes;
-        f16x8 bp[2][2];
+        // transpose operands of a tile: lane (c, g) addresses entry
+        // ks*32 + g*8 + (c >> 1), half (c & 1) of the chunk of dims dbase + 16 dt
+        u32x2 tv[2][kDT];
+        auto read_tv = [&](int j) {
+            const uint8_t *xb = lds + (j % kNB) * L::kBufBytes;
 #pragma unroll
-        for (int nt = 0; nt < 2; nt++)
+            for (int ks = 0; ks < 2; ks++) {
+                const int row = ks * 32 + g * 8 + (c >> 1);
+                const uint8_t *rp = xb + row * kRawBytes + (c & 1) * 8;
+                const int sw = swz<0>(row);
 #pragma unroll
-            for (int ks = 0; ks < 2; ks++)
-                bp[nt][ks] = *reinterpret_cast<const f16x8 *>(p_lds + p_off(nt * 16 + c, 4 * ks + g));
-        bool uneven = false;
-#pragma unroll
-        for (int nt = 0; nt < 2; nt++)
-            uneven |= *reinterpret_cast<const uint32_t *>(
-                          lds + L::kOffFlags + ppar * kHB * 4 + (nt * 16 + c) * 4) != 0x01010101u;
-        if (__ballot(uneven) != 0) {
-            bool any_resc = false;
-            float alpha[2], fq[2][2];
-#pragma unroll
-            for (int nt = 0; nt < 2; nt++) {
-                const float *mrow = mq_lds + (nt * 16 + c) * 4;
-                const f32x4 mq = *reinterpret_cast<const f32x4 *>(mrow);
-                const float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-                const bool resc = mx > m_ref[nt];
-                alpha[nt] = resc ? __builtin_amdgcn_exp2f(m_ref[nt] - mx) : 1.0f;
-                if (resc) m_ref[nt] = mx;
-                any_resc |= resc;
-                fq[nt][0] = __builtin_amdgcn_exp2f(mrow[g >> 1] - m_ref[nt]);
-                fq[nt][1] = __builtin_amdgcn_exp2f(mrow[2 + (g >> 1)] - m_ref[nt]);
+                for (int dt = 0; dt < kDT; dt++)
+                    tv[ks][dt] = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_i32x2 *>(
+                                   LDS_PTR(rp + (((dbase / 16 + dt) ^ sw) * 16)))));
             }
-            if (__ballot(any_resc)) {
+        };
+        // P of tile j (weighted by 2^(m_q - m_ref) while a quarter's maximum
+        // differs from the reference, O rescaled when the reference moves), the
+        // denominator from the operand (wave 4), then the product over the
+        // wave's dims
+        auto pv = [&](int j) {
+            const int ppar = j & 1;
+            const float *mq_lds = reinterpret_cast<const float *>(lds + L::kOffMq + ppar * L::kMqBytes);
+            const uint8_t *p_lds = lds + L::kOffP + ppar * L::kPBytes;
+            f16x8 bp[2][2];
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+                for (int ks = 0; ks < 2; ks++)
+                    bp[nt][ks] = *reinterpret_cast<const f16x8 *>(p_lds + p_off(nt * 16 + c, 4 * ks + g));
+            bool uneven = false;
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++)
+                uneven |= *reinterpret_cast<const uint32_t *>(
+                              lds + L::kOffFlags + ppar * kHB * 4 + (nt * 16 + c) * 4) != 0x01010101u;
+            if (__ballot(uneven) != 0) {
+                bool any_resc = false;
+                float alpha[2], fq[2][2];
 #pragma unroll
                 for (int nt = 0; nt < 2; nt++) {
-#pragma unroll
-                    for (int dt = 0; dt < kDT; dt++) acc[dt][nt] *= alpha[nt];
-                    lacc[nt] *= alpha[nt];
+                    const float *mrow = mq_lds + (nt * 16 + c) * 4;
+                    const f32x4 mq = *reinterpret_cast<const f32x4 *>(mrow);
+                    const float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+                    const bool resc = mx > m_ref[nt];
+                    alpha[nt] = resc ? __builtin_amdgcn_exp2f(m_ref[nt] - mx) : 1.0f;
+                    if (resc) m_ref[nt] = mx;
+                    any_resc |= resc;
+                    fq[nt][0] = __builtin_amdgcn_exp2f(mrow[g >> 1] - m_ref[nt]);
+                    fq[nt][1] = __builtin_amdgcn_exp2f(mrow[2 + (g >> 1)] - m_ref[nt]);
                 }
+                if (__ballot(any_resc)) {
+#pragma unroll
+                    for (int nt = 0; nt < 2; nt++) {
+#pragma unroll
+                        for (int dt = 0; dt < kDT; dt++) acc[dt][nt] *= alpha[nt];
+                        lacc[nt] *= alpha[nt];
+                    }
+                }
+#pragma unroll
+                for (int nt = 0; nt < 2; nt++)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+                        for (int e = 0; e < 8; e++)
+                            bp[nt][ks][e] = (_Float16)((float)bp[nt][ks][e] * fq[nt][ks]);
             }
+            if (w == 4) {
+                const f16x8 one = {1, 1, 1, 1, 1, 1, 1, 1};
 #pragma unroll
-            for (int nt = 0; nt < 2; nt++)
+                for (int nt = 0; nt < 2; nt++)
 #pragma unroll
-                for (int ks = 0; ks < 2; ks++)
-#pragma unroll
-                    for (int e = 0; e < 8; e++)
-                        bp[nt][ks][e] = (_Float16)((float)bp[nt][ks][e] * fq[nt][ks]);
-        }
-        if (w == 4) {
-            const f16x8 one = {1, 1, 1, 1, 1, 1, 1, 1};
-#pragma unroll
-            for (int nt = 0; nt < 2; nt++)
-#pragma unroll
-                for (int ks = 0; ks < 2; ks++)
-                    lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(one, bp[nt][ks], lacc[nt], 0, 0, 0);
-        }
-#pragma unroll
-        for (int dt = 0; dt < kDT; dt++) {
-            const f16x8 av0 = e4m3x8_to_f16(tv[0][dt][0], tv[0][dt][1]);
-            const f16x8 av1 = e4m3x8_to_f16(tv[1][dt][0], tv[1][dt][1]);
-#pragma unroll
-            for (int nt = 0; nt < 2; nt++) {
-                acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, bp[nt][0], acc[dt][nt], 0, 0, 0);
-                acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bp[nt][1], acc[dt][nt], 0, 0, 0);
+                    for (int ks = 0; ks < 2; ks++)
+                        lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(one, bp[nt][ks], lacc[nt], 0, 0, 0);
             }
-        }
-    };
-    barrier_raw();                           // tile 0 and the query copy landed
-    read_tv(0);
-    wait_lgkm0();
-    barrier_raw();                           // (the scoring waves hold the query)
-    for (int k = 0; k < n_tiles; k++) {
-        if (k > 0) {
-            pv(k - 1);
-            read_tv(k);
-        }
-        wait_lgkm0();
-        barrier_raw();
-    }
-    pv(n_tiles - 1);
-
-    // epilogue: wave 4's denominators through LDS, then O / l
-    if (w == 4 && g == 0) {
-#pragma unroll
-        for (int nt = 0; nt < 2; nt++) rl_lds[nt * 16 + c] = lacc[nt][0];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int nt = 0; nt < 2; nt++) {
-        const int hh = nt * 16 + c;
-        const int h = hb * kHB + hh;
-        if (h >= a.H) continue;
-        const float l_tot = rl_lds[hh];
-        const int64_t th = (int64_t)t * a.H + h;
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        if (SPLIT) {
-            const int64_t po = (th * a.n_splits + split) * kD + dbase + 4 * g;
-#pragma unroll
-            for (int dt = 0; dt < kDT; dt++)
-                store_through(reinterpret_cast<f32x4 *>(a.ws + po + dt * 16), acc[dt][nt] * inv);
-            if (w == 4 && g == 0) {
-                float *ml = a.ws + (int64_t)a.T * a.H * a.n_splits * kD + (th * a.n_splits + split) * 2;
-                ml[0] = m_ref[nt];
-                ml[1] = l_tot;
-            }
-        } else {
-            const int64_t base = th * kD + dbase + 4 * g;
 #pragma unroll
             for (int dt = 0; dt < kDT; dt++) {
-                const f32x4 o = acc[dt][nt] * inv;
-                if (OUT_BF16) {
-                    u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                    *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + base + dt * 16) = pk;
-                } else {
-                    *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + base + dt * 16) = o;
+                const f16x8 av0 = e4m3x8_to_f16(tv[0][dt][0], tv[0][dt][1]);
+                const f16x8 av1 = e4m3x8_to_f16(tv[1][dt][0], tv[1][dt][1]);
+#pragma unroll
+                for (int nt = 0; nt < 2; nt++) {
+                    acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av0, bp[nt][0], acc[dt][nt], 0, 0, 0);
+                    acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bp[nt][1], acc[dt][nt], 0, 0, 0);
                 }
             }
-            if (a.lse && w == 4 && g == 0)
-                a.lse[th] = l_tot > 0.0f ? (m_ref[nt] + log2f(l_tot)) * kLn2 : -INFINITY;
+        };
+
+        barrier_raw();                           // tile 0 and the query copy landed
+        read_tv(0);
+        wait_lgkm0();
+        barrier_raw();                           // (the scoring waves hold the query)
+        for (int k = 0; k < n_tiles; k++) {
+            if (k > 0) {
+                pv(k - 1);
+                read_tv(k);
+            }
+            wait_lgkm0();
+            barrier_raw();
         }
+        pv(n_tiles - 1);
+
+        // epilogue: wave 4's denominators through LDS, then O / l
+        if (w == 4 && g == 0) {
+#pragma unroll
+            for (int nt = 0; nt < 2; nt++) rl_lds[nt * 16 + c] = lacc[nt][0];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int nt = 0; nt < 2; nt++) {
+            const int hh = nt * 16 + c;
+            const int h = hb * kHB + hh;
+            if (h >= a.H) continue;
+            const float l_tot = rl_lds[hh];
+            const int64_t th = (int64_t)t * a.H + h;
+            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            if (SPLIT) {
+                const int64_t po = (th * a.n_splits + split) * kD + dbase + 4 * g;
+#pragma unroll
+                for (int dt = 0; dt < kDT; dt++)
+                    store_through(reinterpret_cast<f32x4 *>(a.ws + po + dt * 16), acc[dt][nt] * inv);
+                if (w == 4 && g == 0) {
+                    float *ml = a.ws + (int64_t)a.T * a.H * a.n_splits * kD + (th * a.n_splits + split) * 2;
+                    ml[0] = m_ref[nt];
+                    ml[1] = l_tot;
+                }
+            } else {
+                const int64_t base = th * kD + dbase + 4 * g;
+#pragma unroll
+                for (int dt = 0; dt < kDT; dt++) {
+                    const f32x4 o = acc[dt][nt] * inv;
+                    if (OUT_BF16) {
+                        u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                        *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + base + dt * 16) = pk;
+                    } else {
+                        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + base + dt * 16) = o;
+                    }
+                }
+                if (a.lse && w == 4 && g == 0)
+                    a.lse[th] = l_tot > 0.0f ? (m_ref[nt] + log2f(l_tot)) * kLn2 : -INFINITY;
+            }
+        }
+        vb += gridDim.x;
+        if (!kPersist || !set_unit(vb)) break;
     }
 }
 
@@ -1976,16 +2100,18 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
     const int n_hb = (a.H + kHB - 1) / kHB;
     const dim3 grid((unsigned)(((int64_t)a.T + 7) / 8 * 8 * n_hb * a.n_splits));
     if constexpr (LAYOUT == 0 && NT == 2) {
-        // raw rows in 32-head blocks: the eight-wave kernel
+        // raw rows in 32-head blocks: the eight-wave kernel, whose
+        // workgroups may each take several units (grid_cap)
+        const dim3 grid8(a.grid_cap > 0 && (unsigned)a.grid_cap < grid.x ? (unsigned)a.grid_cap : grid.x);
         if (a.n_splits > 1) {
             constexpr auto kern = attn_w8_kernel<QFP8, OUT_BF16, true>;
             allow_big_lds<kern>(W8::kBytes);
-            kern<<<grid, dim3(W8::kThreads), W8::kBytes, stream>>>(a);
+            kern<<<grid8, dim3(W8::kThreads), W8::kBytes, stream>>>(a);
             launch_combine_s<OUT_BF16>(a, stream);
         } else {
             constexpr auto kern = attn_w8_kernel<QFP8, OUT_BF16, false>;
             allow_big_lds<kern>(W8::kBytes);
-            kern<<<grid, dim3(W8::kThreads), W8::kBytes, stream>>>(a);
+            kern<<<grid8, dim3(W8::kThreads), W8::kBytes, stream>>>(a);
         }
     } else {
         static_assert(NT == 1, "16-head blocks");

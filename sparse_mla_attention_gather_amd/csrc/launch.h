@@ -38,6 +38,8 @@ struct AttnArgs {
     int n_splits;               // splits of the top-k list per (token, head block)
     int split_len;              // entries per split, a multiple of 64
     int32_t *err_count;
+    int grid_cap = 0;           // 32-head blocks: at most this many workgroups,
+                                // each taking several units (0 = one unit each)
 };
 
 // Number of top-k splits for this shape and phase (1 = none) on a device
