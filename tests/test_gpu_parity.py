@@ -269,6 +269,61 @@ def test_fp8_query_32_head_blocks(orc, cfg, phase, od):
         assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
 
 
+# The FP8-query prefill over raw rows runs persistent workgroups (one per
+# compute unit), each taking several (token, head block, split) units in
+# turn and starting the next one (its entries resolved, its first tiles
+# copied) while the current one ends.  Tokens cycle over 5 sequences, so a
+# workgroup's consecutive units read different page-table rows; rows are
+# ragged (1 to 4 tiles, some empty); page-table rows of 63 pages (page size
+# 16, short enough for the first unit to stage in LDS) and of 2000 pages
+# (page size 1).
+@pytest.mark.parametrize("page_size,seq_len", [(16, 1000), (1, 2000)], ids=["short_pt", "long_pt"])
+def test_q8_prefill_persistent_units(orc, page_size, seq_len):
+    T, H, K = 800, 32, 256
+    wl = W.small(261 + page_size, T=T, H=H, K=K, layout=W.RAW, B=5, seq_len=seq_len,
+                 page_size=page_size, neg_frac=0.0)
+    widths = [0, 1, 63, 64, 65, 128, 129, 200, 256]
+    topk = wl.topk.copy()
+    for t in range(T):
+        topk[t, widths[t % len(widths)]:] = -1
+    wl = W.Workload(**{**wl.__dict__, "topk": topk})
+    print(f"case persistent prefill: T={T} H={H} K={K} page_size={page_size} "
+          f"pages={wl.page_table.shape[1]}", flush=True)
+    pool = P.build_pool(orc, wl)
+    di = G.DevInputs(wl)
+    q8_d, sc_d = G.run_quantize(di.q)
+    s_ref = orc.q_scale(wl.q)
+    q8_ref = orc.q_quantize(wl.q, s_ref)
+    assert np.array_equal(G.host(q8_d), q8_ref)
+    ref, ref_lse, ref_err = _oracle_attn(orc, wl, pool, q8_ref, s_ref)
+    out, lse, err = G.run_attn(di, G.dev(pool), phase=1, q=q8_d, q_scale=sc_d)
+    assert err == ref_err == 0
+    G.assert_attn_close(out, ref, where=f"persistent prefill, page size {page_size}")
+    G.assert_lse_close(lse, ref_lse)
+    for t in range(T):
+        if widths[t % len(widths)] == 0:
+            assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
+
+
+def test_q8_prefill_persistent_bad_sequence():
+    """Persistent FP8-query prefill units whose token has a sequence id
+    outside [0, num_seqs) (a workgroup's first and later units) read
+    nothing: output 0, lse -inf, every non -1 entry counted."""
+    T, H, K = 800, 32, 128
+    wl = W.small(265, T=T, H=H, K=K, seq_len=100, page_size=16, B=3)
+    ts = wl.token_seq.copy()
+    bad = [3, 259, 515, 771]
+    ts[bad] = [7, -1, 3, 1 << 20]
+    wl = W.Workload(**{**wl.__dict__, "token_seq": ts})
+    pool = np.zeros((wl.num_slots, 512), np.uint8)
+    di = G.DevInputs(wl)
+    q8_d, sc_d = G.run_quantize(di.q)
+    out, lse, err = G.run_attn(di, G.dev(pool), phase=1, q=q8_d, q_scale=sc_d)
+    for t in bad:
+        assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf), t
+    assert err == int(np.sum(wl.topk[bad] != -1))
+
+
 @pytest.mark.parametrize("H", [16, 32])
 @pytest.mark.parametrize("layout", [W.RAW, W.SCALED, W.ROPE, W.BF16],
                          ids=["raw", "scaled", "rope", "bf16"])
