@@ -1602,18 +1602,30 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
         for (int i = 0; i < kPf; i++)
             phys[i] = a.page_table ? row[min(max(v[i], 0) >> a.page_shift, a.max_pages - 1)] : 0;
         const int sq_len = sq_ok ? __builtin_amdgcn_readfirstlane(sq_len_v) : INT_MAX;
+        // The index rule of resolve_index, for 8 entries of one token: the
+        // token's checks fold into one bound (valid positions are below the
+        // sequence length and below the page table's reach), and nothing is
+        // branched on per entry (a lane's branches cost more than the selects
+        // over 8 entries; this runs while the PV waves finish the unit).
+        const bool has_pt = a.page_table != nullptr;
+        const int lim = !sq_ok ? 0
+                        : has_pt ? (int)min((int64_t)sq_len, (int64_t)a.max_pages << a.page_shift)
+                                 : sq_len;
+        const int pmask = (1 << a.page_shift) - 1;
+        const uint64_t zero_src = reinterpret_cast<uint64_t>(kZeroRow + (16 * q + c) * kRawBytes) | kMaskBits;
         int n_err = 0, last = -1;
 #pragma unroll
         for (int i = 0; i < kPf; i++) {
             const int e = (4 * i + g) * kTile + 16 * q + c;
-            bool err;
-            const int32_t s = resolve_entry(a, v[i], phys[i], sq_ok, sq_len, err);
-            n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(err));
+            const int32_t x = v[i];
+            const int64_t slot = has_pt ? (int64_t)(((uint64_t)(uint32_t)phys[i] << a.page_shift) | (uint32_t)(x & pmask))
+                                        : (int64_t)x;
+            const bool ok = (uint32_t)x < (uint32_t)lim && phys[i] >= 0 && slot < a.num_slots;
+            n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(!ok && x != -1));
             if (e < n_ent_n)
-                slots[e] = s >= 0 ? reinterpret_cast<uint64_t>(a.pool + (int64_t)s * kRawBytes)
-                                  : reinterpret_cast<uint64_t>(kZeroRow + (16 * q + c) * kRawBytes) | kMaskBits;
+                slots[e] = ok ? reinterpret_cast<uint64_t>(a.pool + slot * kRawBytes) : zero_src;
             // the highest tile of step i holding a valid entry
-            const uint64_t bal = __builtin_amdgcn_ballot_w64(e < n_ent_n && s >= 0);
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(e < n_ent_n && ok);
             if (bal) last = (4 * i + ((63 - (int)__builtin_clzll(bal)) >> 4)) * kTile;
         }
         if (lane == 0) {
