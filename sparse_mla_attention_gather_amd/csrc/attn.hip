@@ -228,15 +228,6 @@ __device__ __forceinline__ float sum_over_g(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Index resolution of one entry value i, given the page-table word `phys`
-// already fetched for it (see the prologue).
-__device__ __forceinline__ int32_t resolve_entry(const AttnArgs &a, int32_t i,
-                                                 int32_t phys, bool seq_ok,
-                                                 int seq_len, bool &err) {
-    return resolve_index(i, phys, seq_ok, seq_len, a.page_table != nullptr, a.page_shift,
-                         a.max_pages, a.num_slots, err);
-}
-
 // LDS bank spreading.  A 16-byte-per-lane access serves 16 lanes at a time
 // over the 64 four-byte banks (256 bytes), so the 16 rows c = 0..15 that
 // such an access touches must land on 16 distinct 16-byte positions of a
@@ -566,12 +557,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         // last valid entry of each wave (ballot of the resolved slots; j
         // grows with the lane): the tiles after the split's last valid entry
         // hold only masked entries, which contribute nothing, and are skipped
+        const TokenIndexRule rule(seq_ok, seq_len, a.page_table != nullptr, a.page_shift, a.max_pages,
+                                  a.num_slots);
         int n_err = 0, last = -1;
 #pragma unroll
         for (int i = 0; i < kPer; i++) {
             const int j = tid + i * kThreads;
+            // (a wave past the split's end holds padding only)
+            if (w * 64 + i * kThreads >= n_ent) continue;
             bool err;
-            const int32_t s = resolve_entry(a, v[i], phys[i], seq_ok, seq_len, err);
+            const int32_t s = rule(v[i], phys[i], err);
             n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(err));   // the wave's
             if (j < n_ent)
                 slots[j] = s >= 0 ? reinterpret_cast<uint64_t>(a.pool + (int64_t)s * row_bytes<LAYOUT>())
@@ -1474,12 +1469,16 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
                 for (int i = 0; i < kPer; i++) phys[i] = 0;
             }
         }
+        const TokenIndexRule rule(seq_ok, seq_len, a.page_table != nullptr, a.page_shift, a.max_pages,
+                                  a.num_slots);
         int n_err = 0, last = -1;
 #pragma unroll
         for (int i = 0; i < kPer; i++) {
             const int j = tid + i * L::kThreads;
+            // (a wave past the split's end holds padding only)
+            if (w * 64 + i * L::kThreads >= n_ent) continue;
             bool err;
-            const int32_t s = resolve_entry(a, v[i], phys[i], seq_ok, seq_len, err);
+            const int32_t s = rule(v[i], phys[i], err);
             n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(err));   // the wave's
             if (j < n_ent)
                 slots[j] = s >= 0 ? reinterpret_cast<uint64_t>(a.pool + (int64_t)s * kRawBytes)
@@ -1602,30 +1601,23 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
         for (int i = 0; i < kPf; i++)
             phys[i] = a.page_table ? row[min(max(v[i], 0) >> a.page_shift, a.max_pages - 1)] : 0;
         const int sq_len = sq_ok ? __builtin_amdgcn_readfirstlane(sq_len_v) : INT_MAX;
-        // The index rule of resolve_index, for 8 entries of one token: the
-        // token's checks fold into one bound (valid positions are below the
-        // sequence length and below the page table's reach), and nothing is
-        // branched on per entry (a lane's branches cost more than the selects
-        // over 8 entries; this runs while the PV waves finish the unit).
-        const bool has_pt = a.page_table != nullptr;
-        const int lim = !sq_ok ? 0
-                        : has_pt ? (int)min((int64_t)sq_len, (int64_t)a.max_pages << a.page_shift)
-                                 : sq_len;
-        const int pmask = (1 << a.page_shift) - 1;
+        // (this runs on the unit boundary, while the PV waves finish the unit)
+        const TokenIndexRule rule(sq_ok, sq_len, a.page_table != nullptr, a.page_shift, a.max_pages,
+                                  a.num_slots);
         const uint64_t zero_src = reinterpret_cast<uint64_t>(kZeroRow + (16 * q + c) * kRawBytes) | kMaskBits;
         int n_err = 0, last = -1;
 #pragma unroll
         for (int i = 0; i < kPf; i++) {
             const int e = (4 * i + g) * kTile + 16 * q + c;
-            const int32_t x = v[i];
-            const int64_t slot = has_pt ? (int64_t)(((uint64_t)(uint32_t)phys[i] << a.page_shift) | (uint32_t)(x & pmask))
-                                        : (int64_t)x;
-            const bool ok = (uint32_t)x < (uint32_t)lim && phys[i] >= 0 && slot < a.num_slots;
-            n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(!ok && x != -1));
+            // (entries past the split's end are padding)
+            if (4 * i * kTile >= n_ent_n) continue;
+            bool err;
+            const int32_t s = rule(v[i], phys[i], err);
+            n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(err));
             if (e < n_ent_n)
-                slots[e] = ok ? reinterpret_cast<uint64_t>(a.pool + slot * kRawBytes) : zero_src;
+                slots[e] = s >= 0 ? reinterpret_cast<uint64_t>(a.pool + (int64_t)s * kRawBytes) : zero_src;
             // the highest tile of step i holding a valid entry
-            const uint64_t bal = __builtin_amdgcn_ballot_w64(e < n_ent_n && ok);
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(e < n_ent_n && s >= 0);
             if (bal) last = (4 * i + ((63 - (int)__builtin_clzll(bal)) >> 4)) * kTile;
         }
         if (lane == 0) {

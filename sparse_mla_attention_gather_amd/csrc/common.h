@@ -147,29 +147,41 @@ __device__ __forceinline__ f16x8 e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
     return r;
 }
 
-// Resolution of one top-k entry value i (the attention's prologue and the
-// index transform apply the same rule), given the page-table word `phys`
-// already fetched for it: -1 -> padding (not an error); a negative value, a
-// token whose sequence is invalid, i >= seq_len, a page beyond max_pages or
-// a negative page-table word, or a slot >= num_slots -> masked and counted
-// (`err`).  page_shift = log2(page_size); has_pt false: i is the slot.
-__device__ __forceinline__ int32_t resolve_index(int32_t i, int32_t phys, bool seq_ok,
-                                                 int seq_len, bool has_pt, int page_shift,
-                                                 int max_pages, int64_t num_slots,
-                                                 bool &err) {
-    err = false;
-    if (i == -1) return -1;
-    err = true;
-    if (i < 0 || !seq_ok || i >= seq_len) return -1;
-    int64_t slot = i;
-    if (has_pt) {
-        if ((i >> page_shift) >= max_pages || phys < 0) return -1;
-        slot = ((int64_t)phys << page_shift) | (int64_t)(i & ((1 << page_shift) - 1));
+// Resolution of a token's top-k entry values i (the attention's prologues
+// and the index transform apply the same rule), each given the page-table
+// word `phys` already fetched for it: -1 -> padding (not an error); a
+// negative value, a token whose sequence is invalid, i >= seq_len, a page
+// beyond max_pages or a negative page-table word, or a slot >= num_slots ->
+// masked and counted (`err`).  page_shift = log2(page_size); has_pt false:
+// i is the slot.
+struct TokenIndexRule {
+    uint32_t lim;        // valid positions are below it (0: none)
+    int shift;
+    uint32_t pmask;
+    bool has_pt;
+    int64_t num_slots;
+    // the token's checks folded into one bound: a valid position is below
+    // the sequence length and below the page table's reach, so one unsigned
+    // compare covers i < 0, an invalid sequence, i >= seq_len and a page
+    // beyond max_pages
+    __device__ __forceinline__ TokenIndexRule(bool seq_ok, int seq_len, bool has_pt_, int page_shift,
+                                              int max_pages, int64_t num_slots_)
+        : lim(!seq_ok ? 0u
+                      : (uint32_t)max((int64_t)0, has_pt_ ? min((int64_t)seq_len, (int64_t)max_pages << page_shift)
+                                                          : (int64_t)seq_len)),
+          shift(page_shift), pmask((1u << page_shift) - 1u), has_pt(has_pt_), num_slots(num_slots_) {}
+    // the slot of entry i (phys: its page-table word, unused without a page
+    // table), or -1; err: masked other than as padding.  Nothing is branched
+    // on per entry: callers resolve several entries per lane, where a lane's
+    // branches cost more than the selects.
+    __device__ __forceinline__ int32_t operator()(int32_t i, int32_t phys, bool &err) const {
+        const int64_t slot = has_pt ? (int64_t)(((uint64_t)(uint32_t)phys << shift) | ((uint32_t)i & pmask))
+                                    : (int64_t)i;
+        const bool ok = (uint32_t)i < lim && (!has_pt || phys >= 0) && slot < num_slots;
+        err = !ok && i != -1;
+        return ok ? (int32_t)slot : -1;
     }
-    if (slot >= num_slots) return -1;
-    err = false;
-    return (int32_t)slot;
-}
+};
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {

@@ -6,7 +6,7 @@
 // flattened page table, on the RAGGED path).
 //
 // Each row of top-k positions is resolved with the attention's own rule
-// (resolve_index) and written compacted: the valid physical slots first, in
+// (TokenIndexRule) and written compacted: the valid physical slots first, in
 // their input order, then -1 up to the output width.  The result is the
 // slot list the attention takes with no page table, and its trailing -1
 // tiles are the ones the attention skips.
@@ -42,6 +42,7 @@ __global__ __launch_bounds__(kTThreads) void topk_transform_kernel(TransformArgs
                             ? a.page_table + (int64_t)(seq_ok ? seq : 0) * a.max_pages
                             : nullptr;
     int32_t *out = a.out + t * a.k_out;
+    const TokenIndexRule rule(seq_ok, seq_len, pt != nullptr, a.page_shift, a.max_pages, a.num_slots);
 
     int n = 0, n_err = 0, par = 0;
     for (int j0 = 0; j0 < a.k_in; j0 += kTU * kTThreads, par ^= 1) {
@@ -60,8 +61,7 @@ __global__ __launch_bounds__(kTThreads) void topk_transform_kernel(TransformArgs
 #pragma unroll
         for (int u = 0; u < kTU; u++) {
             bool err;
-            s[u] = resolve_index(v[u], ph[u], seq_ok, seq_len, pt != nullptr, a.page_shift,
-                                 a.max_pages, a.num_slots, err);
+            s[u] = rule(v[u], ph[u], err);
             vm[u] = __builtin_amdgcn_ballot_w64(s[u] >= 0);
             n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(err));
             if (lane == 0) cnt[par][u][w] = __builtin_popcountll(vm[u]);

@@ -539,6 +539,31 @@ def test_out_of_range_sequence_id():
     assert err == int(np.sum(wl.topk[2] != -1))
 
 
+@pytest.mark.parametrize("kind", ["decode", "prefill", "q8_prefill_persistent"])
+def test_negative_sequence_length(kind):
+    """A sequence whose length is negative holds no valid position: every
+    non -1 entry of its tokens is masked and counted, output 0, lse -inf.
+    Covers the 16-head kernel (decode, prefill) and the persistent FP8-query
+    prefill (tokens of that sequence in a workgroup's first and later
+    units)."""
+    H, T = (32, 800) if kind == "q8_prefill_persistent" else (16, 9)
+    wl = W.small(304, T=T, H=H, K=128, seq_len=100, page_size=16, B=3)
+    sl = wl.seq_lens.copy()
+    sl[1] = -5
+    wl = W.Workload(**{**wl.__dict__, "seq_lens": sl})
+    pool = np.zeros((wl.num_slots, 512), np.uint8)
+    di = G.DevInputs(wl)
+    kw = {}
+    if kind == "q8_prefill_persistent":
+        q8_d, sc_d = G.run_quantize(di.q)
+        kw = dict(q=q8_d, q_scale=sc_d)
+    out, lse, err = G.run_attn(di, G.dev(pool), phase=0 if kind == "decode" else 1, **kw)
+    bad = np.nonzero(wl.token_seq == 1)[0]
+    for t in bad:
+        assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf), t
+    assert err == int(np.sum(wl.topk[bad] != -1))
+
+
 @pytest.mark.parametrize("prefix,T,K", [(200, 300, 256), (0, 260, 256)])
 def test_prefill_pipeline_live_tail(orc, prefix, T, K):
     """Writer -> query quantisation -> prefill, in stream order: the top-k
