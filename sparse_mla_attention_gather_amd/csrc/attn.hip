@@ -1557,7 +1557,7 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
     // words and token are loaded during the last scoring step
     // (fetch_next), its page-table words, resolution and slot array follow
     // the loop (start_next), and each scoring wave then issues its share of
-    // the next query copy and its rows of the next unit's first three tiles.
+    // the next query copy and its rows of the next unit's first two tiles.
     // After the last step no wave reads a tile buffer or the slot array any
     // more, so all four buffers are free.  Lane (c, g) of wave q resolves
     // entries (4 i + g) * 64 + 16 q + c (i < 8): the rows that wave q copies
@@ -1629,13 +1629,13 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
         asm volatile("" ::: "memory");
         issue_q(tn, hbn);
 #pragma unroll
-        for (int j = 0; j < 3; j++)
+        for (int j = 0; j < 2; j++)
             if (j * kTile < n_ent_n) issue_tile8(j);
     };
 
     if (__builtin_amdgcn_readfirstlane((int)is_v) == 0) {
         // ================= scoring waves =================
-        // (from the second unit on, the query copy and tiles 0-2 were issued
+        // (from the second unit on, the query copy and tiles 0-1 were issued
         // at the end of the previous one)
         for (int vb = blockIdx.x, pref = 0;; pref = 1) {
             read_n_tiles();
@@ -1644,7 +1644,7 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
                 issue_tile8(0);
                 if (n_tiles > 1) issue_tile8(1);
             }
-            wait_own(0, pref ? 2 : 1);
+            wait_own(0, 1);
             barrier_raw();                       // tile 0 and the query copy landed
             // The query of both head tiles as the B operand.  FP8:
             // bq8[nt][k2] = q8[h][128 k2 + 32 g .. +32] (chunks 8 k2 + 2g, +1);
@@ -1690,7 +1690,7 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
                 }
             };
             read_xc(0);
-            if (!pref && n_tiles > 2) issue_tile8(2);
+            if (n_tiles > 2) issue_tile8(2);
             wait_lgkm0();
             barrier_raw();                       // every scoring wave holds the query
             if (n_tiles > 3) issue_tile8(3);
