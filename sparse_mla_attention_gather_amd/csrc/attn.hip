@@ -268,6 +268,11 @@ __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(gptr), "s"(lds_base) : "memory", "m0");
 }
+// The same with 4 bytes per lane (lane l's word lands at lds_base + 4 l).
+__device__ __forceinline__ void dma4(const void *gptr, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(gptr), "s"(lds_base) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // A 16- or 8-byte global store written through to device scope (sc1), so
@@ -1366,7 +1371,12 @@ struct W8 {
     static constexpr int kOffRedL = kOffMq + 2 * kMqBytes;     // last entries, then denominators
     static constexpr int kOffFlags = kOffRedL + kHB * 16;      // [32][4] bytes, two
     static constexpr int kOffLast = kOffFlags + 2 * kHB * 4;   // a unit's last valid entries [8]
-    static constexpr int kBytes = kOffLast + 8 * 4;
+    // persistent workgroups: the next unit's page-table row (when it fits),
+    // its sequence length (64 copies) and its sequence
+    static constexpr int kOffPtN = kOffLast + 8 * 4;
+    static constexpr int kPtNCap = 1472;
+    static constexpr int kOffSeqN = kOffPtN + kPtNCap * 4;
+    static constexpr int kBytes = kOffSeqN + 64 * 4 + 16;
     static constexpr int kDT = 8;                              // PV: 16-dim tiles per wave
     static constexpr int kLoads = 8;                           // DMA instructions per scoring wave and tile
     // the page-table row is staged in tile buffer 2 (free until after the prologue)
@@ -1552,16 +1562,19 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
         return reinterpret_cast<const u32x4 *>(qst + hl * kQRowBytes + ((chunk ^ (hl & 7)) << 4));
     };
 
-    // The next unit (virtual block vn), started by the scoring waves while
-    // the PV waves run the unit's last tile and write its output: its top-k
-    // words and token are loaded during the last scoring step
-    // (fetch_next), its page-table words, resolution and slot array follow
-    // the loop (start_next), and each scoring wave then issues its share of
-    // the next query copy and its rows of the next unit's first two tiles.
-    // After the last step no wave reads a tile buffer or the slot array any
-    // more, so all four buffers are free.  Lane (c, g) of wave q resolves
-    // entries (4 i + g) * 64 + 16 q + c (i < 8): the rows that wave q copies
-    // in every tile, so that its copies read only slots it wrote itself.
+    // The next unit (virtual block vn) is started while the current one
+    // ends: its token's sequence is read at the unit's start, and once the
+    // query is taken that sequence's length and page-table row (when it
+    // fits) are copied into LDS, where they wait through the unit with no
+    // register held; its top-k words are loaded during each role's last
+    // step (fetch_next) and resolved into the slot array after it
+    // (resolve_next), half by each role; the scoring waves then issue their
+    // shares of the next query copy and their rows of the next unit's first
+    // two tiles.  After the last step no wave reads a tile buffer or the
+    // slot array any more, so all four buffers are free.  Lane (c, g) of
+    // scoring wave q (and of PV wave 4 + q) resolves entries
+    // (4 i + g) * 64 + 16 q + c: the rows that scoring wave q copies in
+    // every tile, so that its copies read only slots it wrote itself.
     constexpr int kPf = kMaxSplit / (4 * kTile);
     auto next_coords = [&](int vn, int &tn, int &hbn, int &begin_n, int &n_ent_n) {
         const int kqn = vn >> 3;
@@ -1571,61 +1584,87 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
         n_ent_n = min(a.K - begin_n, a.split_len);
         return vn < n_virt && tn < a.T;
     };
-    auto fetch_next = [&](int vn, int32_t (&v)[kPf], int32_t &seq_v) {
+    const int32_t *const seq_n_lds = reinterpret_cast<const int32_t *>(lds + L::kOffSeqN);
+    auto seq_ok_of = [&](int sq) {
+        return (a.page_table == nullptr && a.seq_lens == nullptr) || (sq >= 0 && sq < a.num_seqs);
+    };
+    const bool pt_n_fits = a.page_table != nullptr && a.max_pages <= L::kPtNCap;
+    // the next unit's sequence length and page-table row into LDS (scoring
+    // waves, once the query is taken; landed, like every copy, by the
+    // next-to-last step's wait, or the last step's in a one-tile unit)
+    auto stage_next = [&](int sq) {
+        const bool sq_ok = seq_ok_of(sq);
+        if (pt_n_fits) {
+            const int32_t *row = a.page_table + (int64_t)(sq_ok ? sq : 0) * a.max_pages;
+            for (int m = q; m * 64 < a.max_pages; m += 4)
+                dma4(row + min(m * 64 + lane, a.max_pages - 1), lds0 + L::kOffPtN + m * 256);
+        }
+        if (q == 0) {
+            if (a.seq_lens && sq_ok) dma4(a.seq_lens + sq, lds0 + L::kOffSeqN);
+            if (lane == 0) reinterpret_cast<int32_t *>(lds + L::kOffSeqN)[64] = sq;
+        }
+    };
+    // The next unit's entries in two halves: chunks 0-3 (tiles 0-15) by the
+    // scoring waves, whose copies of tiles 0 and 1 follow, and chunks 4-7
+    // (tiles 16-31) by the PV waves once their last tile is done; wave 4 + q
+    // takes quarter q like scoring wave q.  Words are loaded during the
+    // role's last step (fetch_next) and resolved after it (resolve_next).
+    constexpr int kHalf = kPf / 2;
+    auto fetch_next = [&](int vn, int qq, int i0, int32_t (&v)[kHalf]) {
         int tn, hbn, begin_n, n_ent_n;
         next_coords(vn, tn, hbn, begin_n, n_ent_n);
         const int32_t *tk = a.topk + (int64_t)tn * a.K + begin_n;
 #pragma unroll
-        for (int i = 0; i < kPf; i++) {
-            const int e = (4 * i + g) * kTile + 16 * q + c;
+        for (int ii = 0; ii < kHalf; ii++) {
+            const int e = (4 * (i0 + ii) + g) * kTile + 16 * qq + c;
             const int32_t xv = tk[min(e, n_ent_n - 1)];
-            v[i] = e < n_ent_n ? xv : -1;
+            v[ii] = e < n_ent_n ? xv : -1;
         }
-        // a vector load (the token is uniform): the step's LDS waits then do
-        // not wait for it
-        int tsel = tn;
-        asm volatile("" : "+v"(tsel));
-        seq_v = a.token_seq ? a.token_seq[tsel] : tsel;
     };
-    auto start_next = [&](int vn, const int32_t (&v)[kPf], int32_t seq_v) {
+    auto resolve_next = [&](int vn, int qq, int i0, const int32_t (&v)[kHalf]) {
         int tn, hbn, begin_n, n_ent_n;
         next_coords(vn, tn, hbn, begin_n, n_ent_n);
-        const int sq = __builtin_amdgcn_readfirstlane(seq_v);
-        const bool sq_ok = (a.page_table == nullptr && a.seq_lens == nullptr) || (sq >= 0 && sq < a.num_seqs);
-        const int32_t *row = a.page_table + (int64_t)(sq_ok ? sq : 0) * a.max_pages;
-        int32_t phys[kPf];
-        int ssel = sq_ok ? sq : 0;
-        asm volatile("" : "+v"(ssel));
-        const int sq_len_v = (a.seq_lens && sq_ok) ? a.seq_lens[ssel] : INT_MAX;
+        const int sq = __builtin_amdgcn_readfirstlane(seq_n_lds[64]);
+        const bool sq_ok = seq_ok_of(sq);
+        const int sq_len = (a.seq_lens && sq_ok) ? __builtin_amdgcn_readfirstlane(seq_n_lds[0]) : INT_MAX;
+        int32_t phys[kHalf];
+        if (pt_n_fits) {
+            const int32_t *pt_n = reinterpret_cast<const int32_t *>(lds + L::kOffPtN);
 #pragma unroll
-        for (int i = 0; i < kPf; i++)
-            phys[i] = a.page_table ? row[min(max(v[i], 0) >> a.page_shift, a.max_pages - 1)] : 0;
-        const int sq_len = sq_ok ? __builtin_amdgcn_readfirstlane(sq_len_v) : INT_MAX;
-        // (this runs on the unit boundary, while the PV waves finish the unit)
+            for (int ii = 0; ii < kHalf; ii++) phys[ii] = pt_n[min(max(v[ii], 0) >> a.page_shift, a.max_pages - 1)];
+        } else {
+            const int32_t *row = a.page_table + (int64_t)(sq_ok ? sq : 0) * a.max_pages;
+#pragma unroll
+            for (int ii = 0; ii < kHalf; ii++)
+                phys[ii] = a.page_table ? row[min(max(v[ii], 0) >> a.page_shift, a.max_pages - 1)] : 0;
+        }
         const TokenIndexRule rule(sq_ok, sq_len, a.page_table != nullptr, a.page_shift, a.max_pages,
                                   a.num_slots);
-        const uint64_t zero_src = reinterpret_cast<uint64_t>(kZeroRow + (16 * q + c) * kRawBytes) | kMaskBits;
+        const uint64_t zero_src = reinterpret_cast<uint64_t>(kZeroRow + (16 * qq + c) * kRawBytes) | kMaskBits;
         int n_err = 0, last = -1;
 #pragma unroll
-        for (int i = 0; i < kPf; i++) {
-            const int e = (4 * i + g) * kTile + 16 * q + c;
-            // (entries past the split's end are padding)
+        for (int ii = 0; ii < kHalf; ii++) {
+            const int i = i0 + ii;
+            // (a chunk past the split's end holds padding only; past it
+            // within a chunk, v is -1 and the slot a zero row, never read)
             if (4 * i * kTile >= n_ent_n) continue;
+            const int e = (4 * i + g) * kTile + 16 * qq + c;
             bool err;
-            const int32_t s = rule(v[i], phys[i], err);
+            const int32_t sl = rule(v[ii], phys[ii], err);
             n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(err));
-            if (e < n_ent_n)
-                slots[e] = s >= 0 ? reinterpret_cast<uint64_t>(a.pool + (int64_t)s * kRawBytes) : zero_src;
-            // the highest tile of step i holding a valid entry
-            const uint64_t bal = __builtin_amdgcn_ballot_w64(e < n_ent_n && s >= 0);
+            slots[e] = sl >= 0 ? reinterpret_cast<uint64_t>(a.pool + (int64_t)sl * kRawBytes) : zero_src;
+            // the highest tile of chunk i holding a valid entry
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(sl >= 0);
             if (bal) last = (4 * i + ((63 - (int)__builtin_clzll(bal)) >> 4)) * kTile;
         }
-        if (lane == 0) {
-            last_lds[w] = last;
-            last_lds[w + 4] = -1;
-        }
+        if (lane == 0) last_lds[w] = last;
         if (a.err_count && hbn == 0 && lane == 0 && n_err) atomicAdd(a.err_count, n_err);
-        // (the copies below read this wave's own slot stores, in order)
+    };
+    // scoring waves, after their half: the next query copy and this wave's
+    // rows of tiles 0 and 1 (reading its own slot stores, in order)
+    auto issue_next = [&](int vn) {
+        int tn, hbn, begin_n, n_ent_n;
+        next_coords(vn, tn, hbn, begin_n, n_ent_n);
         asm volatile("" ::: "memory");
         issue_q(tn, hbn);
 #pragma unroll
@@ -1639,6 +1678,16 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
         // at the end of the previous one)
         for (int vb = blockIdx.x, pref = 0;; pref = 1) {
             read_n_tiles();
+            // the next unit and its token's sequence (a scalar load, waited
+            // for with tile 0)
+            const int vn = vb + (int)gridDim.x;
+            bool has_next = false;
+            int sq_n = 0;
+            if (kPersist) {
+                int tn, hbn, begin_n, n_ent_n;
+                has_next = next_coords(vn, tn, hbn, begin_n, n_ent_n);
+                if (has_next) sq_n = a.token_seq ? a.token_seq[tn] : tn;
+            }
             if (!pref) {
                 issue_q(t, hb);
                 issue_tile8(0);
@@ -1694,6 +1743,7 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
             wait_lgkm0();
             barrier_raw();                       // every scoring wave holds the query
             if (n_tiles > 3) issue_tile8(3);
+            if (has_next) stage_next(sq_n);
 
             float m_own[2] = {kNoMax, kNoMax};
             // this lane's LDS addresses in the step, less their per-tile parts
@@ -1705,17 +1755,11 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
             float *const mq_l = reinterpret_cast<float *>(lds + L::kOffMq) + c * 4 + q;
             const f32x4 *const mp_l = reinterpret_cast<const f32x4 *>(lds + L::kOffMq) + c;
             uint8_t *const p_l = lds + L::kOffP + p_off(c, 2 * q + (g >> 1)) + (g & 1) * 8;
-            const int vn = vb + (int)gridDim.x;
-            bool has_next = false;
-            if (kPersist) {
-                int tn, hbn, begin_n, n_ent_n;
-                has_next = next_coords(vn, tn, hbn, begin_n, n_ent_n);
-            }
-            int32_t nwords[kPf], nseq = 0;
+            int32_t nwords[kHalf];
             // one step: the last one apart (last_step), so that the next
             // unit's words are live only from there on
             auto step = [&](const int k, const bool last_step) {
-                if (last_step && has_next) fetch_next(vn, nwords, nseq);
+                if (last_step && has_next) fetch_next(vn, q, 0, nwords);
                 // row sources of the tile that refills this step's buffer
                 const int nx = k + kNB;
                 uint64_t nsrc[L::kLoads];
@@ -1798,13 +1842,19 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
                         u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
                     if (g == 0) mq_l[par * (L::kMqBytes / 4) + nt * 64] = m_own[nt];
                 }
-                wait_lgkm0();
+                // (in a one-tile unit the next unit's staging copies, issued
+                // after the query was taken, have had no wait yet)
+                if (last_step && n_tiles == 1) wait_vm_lgkm0<0>();
+                else wait_lgkm0();
                 barrier_raw();
                 if (!last_step && nx < n_tiles) issue(nx, nsrc);
             };
             for (int k = 0; k < n_tiles - 1; k++) step(k, false);
             step(n_tiles - 1, true);
-            if (has_next) start_next(vn, nwords, nseq);
+            if (has_next) {
+                resolve_next(vn, q, 0, nwords);
+                issue_next(vn);
+            }
             __syncthreads();                 // the PV waves' epilogue barrier
             vb = vn;
             if (!kPersist || !set_unit(vb)) break;
@@ -1815,6 +1865,13 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
     // ================= PV waves =================
     for (int vb = blockIdx.x;;) {
         read_n_tiles();
+        const int vn = vb + (int)gridDim.x;
+        bool has_next = false;
+        if (kPersist) {
+            int tn, hbn, begin_n, n_ent_n;
+            has_next = next_coords(vn, tn, hbn, begin_n, n_ent_n);
+        }
+        int32_t nwords[kHalf];
         f32x4 acc[kDT][2], lacc[2];
         float m_ref[2] = {kNoMax, kNoMax};
 #pragma unroll
@@ -1919,10 +1976,12 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
                 pv(k - 1);
                 read_tv(k);
             }
+            if (has_next && k == n_tiles - 1) fetch_next(vn, w - 4, kHalf, nwords);
             wait_lgkm0();
             barrier_raw();
         }
         pv(n_tiles - 1);
+        if (has_next) resolve_next(vn, w - 4, kHalf, nwords);
 
         // epilogue: wave 4's denominators through LDS, then O / l
         if (w == 4 && g == 0) {
@@ -1964,7 +2023,7 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
                     a.lse[th] = l_tot > 0.0f ? (m_ref[nt] + log2f(l_tot)) * kLn2 : -INFINITY;
             }
         }
-        vb += gridDim.x;
+        vb = vn;
         if (!kPersist || !set_unit(vb)) break;
     }
 }
