@@ -275,6 +275,33 @@ __device__ __forceinline__ void dma4(const void *gptr, uint32_t lds_base) {
 }
 #pragma clang diagnostic pop
 
+// bf16 outputs of a head tile's row segment.  Lane (c, g) holds, for each
+// 16-dim tile dt, dims 16 dt + 4g .. +4 of head row c (o(dt), fp32).  For
+// each pair of dim tiles, lanes of even g take dim tile 2m (their own 4 dims
+// and those of lane g + 1), lanes of odd g dim tile 2m + 1 (those of lane
+// g - 1 and their own), exchanged with one 16-lane row swap per word; a
+// 16-byte store then covers 64 contiguous bytes of each of the 16 rows
+// (8-byte stores of each lane's own dims: 32 bytes per row and twice the
+// instructions).  row: the head row's first dim of this segment.
+template <int kDT, typename F>
+__device__ __forceinline__ void store_bf16_tiles(uint16_t *row, int g, F &&o) {
+    static_assert(kDT % 2 == 0, "dim tiles in pairs");
+#pragma unroll
+    for (int m = 0; m < kDT / 2; m++) {
+        const f32x4 o0 = o(2 * m), o1 = o(2 * m + 1);
+        uint32_t p0[2] = {pack_bf16x2(o0[0], o0[1]), pack_bf16x2(o0[2], o0[3])};
+        uint32_t p1[2] = {pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3])};
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(p0[k], p1[k], false, false);
+            p0[k] = sw[0];
+            p1[k] = sw[1];
+        }
+        const int d0 = (2 * m + (g & 1)) * 16 + 4 * (g & 2);
+        *reinterpret_cast<u32x4 *>(row + d0) = u32x4{p0[0], p0[1], p1[0], p1[1]};
+    }
+}
+
 // A 16- or 8-byte global store written through to device scope (sc1), so
 // that the line is not left dirty in this XCD's L2 for the write-back that
 // ends the kernel; the decode's split partials otherwise put that write-back
@@ -1204,16 +1231,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 }
             } else {
                 const float inv = (l_tot > 0.0f ? 1.0f / l_tot : 0.0f) * (kScaled ? s_ref : 1.0f);
-                const int64_t base = th * kD + dbase + 4 * g;
+                if (OUT_BF16) {
+                    store_bf16_tiles<kDT>(reinterpret_cast<uint16_t *>(a.out) + th * kD + dbase, g,
+                                          [&](int dt) { return acc[dt][nt] * inv; });
+                } else {
+                    const int64_t base = th * kD + dbase + 4 * g;
 #pragma unroll
-                for (int dt = 0; dt < kDT; dt++) {
-                    const f32x4 o = acc[dt][nt] * inv;
-                    if (OUT_BF16) {
-                        u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                        *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + base + dt * 16) = pk;
-                    } else {
-                        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + base + dt * 16) = o;
-                    }
+                    for (int dt = 0; dt < kDT; dt++)
+                        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + base + dt * 16) = acc[dt][nt] * inv;
                 }
                 if (a.lse && w == w_first && g == 0)
                     a.lse[th] = l_tot > 0.0f ? (m_ref[nt] + log2f(l_tot)) * kLn2 : -INFINITY;
@@ -2009,28 +2034,8 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
                 }
             } else {
                 if (OUT_BF16) {
-                    // 16-byte stores: for each pair of dim tiles, lanes of
-                    // even g take dim tile 2m (their own 4 dims and those of
-                    // lane g + 1), lanes of odd g dim tile 2m + 1 (those of
-                    // lane g - 1 and their own), exchanged with one 16-lane
-                    // row swap per word; a store then covers 64 contiguous
-                    // bytes of each of 16 head rows (8-byte stores: half the
-                    // bytes per row, twice the instructions)
-                    uint16_t *const orow = reinterpret_cast<uint16_t *>(a.out) + th * kD + dbase;
-#pragma unroll
-                    for (int m = 0; m < kDT / 2; m++) {
-                        const f32x4 o0 = acc[2 * m][nt] * inv, o1 = acc[2 * m + 1][nt] * inv;
-                        uint32_t p0[2] = {pack_bf16x2(o0[0], o0[1]), pack_bf16x2(o0[2], o0[3])};
-                        uint32_t p1[2] = {pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3])};
-#pragma unroll
-                        for (int k = 0; k < 2; k++) {
-                            const auto sw = __builtin_amdgcn_permlane16_swap(p0[k], p1[k], false, false);
-                            p0[k] = sw[0];
-                            p1[k] = sw[1];
-                        }
-                        const int d0 = (2 * m + (g & 1)) * 16 + 4 * (g & 2);
-                        *reinterpret_cast<u32x4 *>(orow + d0) = u32x4{p0[0], p0[1], p1[0], p1[1]};
-                    }
+                    store_bf16_tiles<kDT>(reinterpret_cast<uint16_t *>(a.out) + th * kD + dbase, g,
+                                          [&](int dt) { return acc[dt][nt] * inv; });
                 } else {
                     const int64_t base = th * kD + dbase + 4 * g;
 #pragma unroll
