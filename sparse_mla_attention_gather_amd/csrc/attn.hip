@@ -1433,17 +1433,28 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
     // the previous one (resolve_next), so that its start needs no prologue.
     const int per_tok = n_hb * a.n_splits;
     const int n_virt = (a.T + 7) / 8 * 8 * per_tok;
-    int t = 0, hb = 0, split = 0, begin = 0, n_ent = 0;   // the current unit
-    auto set_unit = [&](int v) {
+    struct Unit { int t, hb, split, begin, n_ent; bool valid; };
+    auto unit_at = [&](int v) {
+        Unit u;
         const int kqv = v >> 3;
-        t = (kqv / per_tok) * 8 + (v & 7);
-        hb = (kqv % per_tok) / a.n_splits;
-        split = kqv % a.n_splits;
-        begin = split * a.split_len;
-        n_ent = min(a.K - begin, a.split_len);   // a multiple of 64
-        return v < n_virt && t < a.T;            // (past the last token, so is every later one)
+        u.t = (kqv / per_tok) * 8 + (v & 7);
+        u.hb = (kqv % per_tok) / a.n_splits;
+        u.split = kqv % a.n_splits;
+        u.begin = u.split * a.split_len;
+        u.n_ent = min(a.K - u.begin, a.split_len);   // a multiple of 64
+        u.valid = v < n_virt && u.t < a.T;          // (past the last token, so is every later one)
+        return u;
     };
-    if (!set_unit(blockIdx.x)) return;
+    int t = 0, hb = 0, split = 0, begin = 0, n_ent = 0;   // the current unit
+    auto set_unit = [&](const Unit &u) {
+        t = u.t;
+        hb = u.hb;
+        split = u.split;
+        begin = u.begin;
+        n_ent = u.n_ent;
+        return u.valid;
+    };
+    if (!set_unit(unit_at(blockIdx.x))) return;
     // (several units per workgroup with an FP8 query only: with a bf16 query
     // the scoring waves' registers leave no room for the unit loop)
     constexpr bool kPersist = QFP8;
@@ -1601,14 +1612,6 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
     // (4 i + g) * 64 + 16 q + c: the rows that scoring wave q copies in
     // every tile, so that its copies read only slots it wrote itself.
     constexpr int kPf = kMaxSplit / (4 * kTile);
-    auto next_coords = [&](int vn, int &tn, int &hbn, int &begin_n, int &n_ent_n) {
-        const int kqn = vn >> 3;
-        tn = (kqn / per_tok) * 8 + (vn & 7);
-        hbn = (kqn % per_tok) / a.n_splits;
-        begin_n = (kqn % a.n_splits) * a.split_len;
-        n_ent_n = min(a.K - begin_n, a.split_len);
-        return vn < n_virt && tn < a.T;
-    };
     const int32_t *const seq_n_lds = reinterpret_cast<const int32_t *>(lds + L::kOffSeqN);
     auto seq_ok_of = [&](int sq) {
         return (a.page_table == nullptr && a.seq_lens == nullptr) || (sq >= 0 && sq < a.num_seqs);
@@ -1635,10 +1638,10 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
     // takes quarter q like scoring wave q.  Words are loaded during the
     // role's last step (fetch_next) and resolved after it (resolve_next).
     constexpr int kHalf = kPf / 2;
-    auto fetch_next = [&](int vn, int qq, int i0, int32_t (&v)[kHalf]) {
-        int tn, hbn, begin_n, n_ent_n;
-        next_coords(vn, tn, hbn, begin_n, n_ent_n);
-        const int32_t *tk = a.topk + (int64_t)tn * a.K + begin_n;
+    // (nu: the next unit, computed once at the unit's start)
+    auto fetch_next = [&](const Unit &nu, int qq, int i0, int32_t (&v)[kHalf]) {
+        const int n_ent_n = nu.n_ent;
+        const int32_t *tk = a.topk + (int64_t)nu.t * a.K + nu.begin;
 #pragma unroll
         for (int ii = 0; ii < kHalf; ii++) {
             const int e = (4 * (i0 + ii) + g) * kTile + 16 * qq + c;
@@ -1646,9 +1649,8 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
             v[ii] = e < n_ent_n ? xv : -1;
         }
     };
-    auto resolve_next = [&](int vn, int qq, int i0, const int32_t (&v)[kHalf]) {
-        int tn, hbn, begin_n, n_ent_n;
-        next_coords(vn, tn, hbn, begin_n, n_ent_n);
+    auto resolve_next = [&](const Unit &nu, int qq, int i0, const int32_t (&v)[kHalf]) {
+        const int n_ent_n = nu.n_ent;
         const int sq = __builtin_amdgcn_readfirstlane(seq_n_lds[64]);
         const bool sq_ok = seq_ok_of(sq);
         const int sq_len = (a.seq_lens && sq_ok) ? __builtin_amdgcn_readfirstlane(seq_n_lds[0]) : INT_MAX;
@@ -1683,18 +1685,16 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
             if (bal) last = (4 * i + ((63 - (int)__builtin_clzll(bal)) >> 4)) * kTile;
         }
         if (lane == 0) last_lds[w] = last;
-        if (a.err_count && hbn == 0 && lane == 0 && n_err) atomicAdd(a.err_count, n_err);
+        if (a.err_count && nu.hb == 0 && lane == 0 && n_err) atomicAdd(a.err_count, n_err);
     };
     // scoring waves, after their half: the next query copy and this wave's
     // rows of tiles 0 and 1 (reading its own slot stores, in order)
-    auto issue_next = [&](int vn) {
-        int tn, hbn, begin_n, n_ent_n;
-        next_coords(vn, tn, hbn, begin_n, n_ent_n);
+    auto issue_next = [&](const Unit &nu) {
         asm volatile("" ::: "memory");
-        issue_q(tn, hbn);
+        issue_q(nu.t, nu.hb);
 #pragma unroll
         for (int j = 0; j < 2; j++)
-            if (j * kTile < n_ent_n) issue_tile8(j);
+            if (j * kTile < nu.n_ent) issue_tile8(j);
     };
 
     if (__builtin_amdgcn_readfirstlane((int)is_v) == 0) {
@@ -1706,13 +1706,10 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
             // the next unit and its token's sequence (a scalar load, waited
             // for with tile 0)
             const int vn = vb + (int)gridDim.x;
-            bool has_next = false;
+            const Unit nu = kPersist ? unit_at(vn) : Unit{0, 0, 0, 0, 0, false};
+            const bool has_next = kPersist && nu.valid;
             int sq_n = 0;
-            if (kPersist) {
-                int tn, hbn, begin_n, n_ent_n;
-                has_next = next_coords(vn, tn, hbn, begin_n, n_ent_n);
-                if (has_next) sq_n = a.token_seq ? a.token_seq[tn] : tn;
-            }
+            if (has_next) sq_n = a.token_seq ? a.token_seq[nu.t] : nu.t;
             if (!pref) {
                 issue_q(t, hb);
                 issue_tile8(0);
@@ -1784,7 +1781,7 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
             // one step: the last one apart (last_step), so that the next
             // unit's words are live only from there on
             auto step = [&](const int k, const bool last_step) {
-                if (last_step && has_next) fetch_next(vn, q, 0, nwords);
+                if (last_step && has_next) fetch_next(nu, q, 0, nwords);
                 // row sources of the tile that refills this step's buffer
                 const int nx = k + kNB;
                 uint64_t nsrc[L::kLoads];
@@ -1877,12 +1874,13 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
             for (int k = 0; k < n_tiles - 1; k++) step(k, false);
             step(n_tiles - 1, true);
             if (has_next) {
-                resolve_next(vn, q, 0, nwords);
-                issue_next(vn);
+                resolve_next(nu, q, 0, nwords);
+                issue_next(nu);
             }
             __syncthreads();                 // the PV waves' epilogue barrier
             vb = vn;
-            if (!kPersist || !set_unit(vb)) break;
+            if (!has_next) break;
+            set_unit(nu);
         }
         return;
     }
@@ -1891,11 +1889,8 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
     for (int vb = blockIdx.x;;) {
         read_n_tiles();
         const int vn = vb + (int)gridDim.x;
-        bool has_next = false;
-        if (kPersist) {
-            int tn, hbn, begin_n, n_ent_n;
-            has_next = next_coords(vn, tn, hbn, begin_n, n_ent_n);
-        }
+        const Unit nu = kPersist ? unit_at(vn) : Unit{0, 0, 0, 0, 0, false};
+        const bool has_next = kPersist && nu.valid;
         int32_t nwords[kHalf];
         f32x4 acc[kDT][2], lacc[2];
         float m_ref[2] = {kNoMax, kNoMax};
@@ -2001,12 +1996,12 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
                 pv(k - 1);
                 read_tv(k);
             }
-            if (has_next && k == n_tiles - 1) fetch_next(vn, w - 4, kHalf, nwords);
+            if (has_next && k == n_tiles - 1) fetch_next(nu, w - 4, kHalf, nwords);
             wait_lgkm0();
             barrier_raw();
         }
         pv(n_tiles - 1);
-        if (has_next) resolve_next(vn, w - 4, kHalf, nwords);
+        if (has_next) resolve_next(nu, w - 4, kHalf, nwords);
 
         // epilogue: wave 4's denominators through LDS, then O / l
         if (w == 4 && g == 0) {
@@ -2047,7 +2042,8 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
             }
         }
         vb = vn;
-        if (!kPersist || !set_unit(vb)) break;
+        if (!has_next) break;
+        set_unit(nu);
     }
 }
 
