@@ -305,6 +305,35 @@ def test_q8_prefill_persistent_units(orc, page_size, seq_len):
             assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
 
 
+def test_q8_prefill_persistent_splits(orc):
+    """Persistent FP8-query prefill units of a top-k list longer than one
+    split (2304 entries: two splits per token, their partial states merged
+    afterwards), several units per workgroup, ragged rows up to the full
+    width."""
+    T, H, K = 400, 32, 2304
+    wl = W.small(264, T=T, H=H, K=K, layout=W.RAW, B=3, seq_len=3000, page_size=16,
+                 neg_frac=0.0)
+    widths = [0, 64, 700, 1200, 2100, 2304]
+    topk = wl.topk.copy()
+    for t in range(T):
+        topk[t, widths[t % len(widths)]:] = -1
+    wl = W.Workload(**{**wl.__dict__, "topk": topk})
+    print(f"case persistent prefill with splits: T={T} H={H} K={K}", flush=True)
+    pool = P.build_pool(orc, wl)
+    di = G.DevInputs(wl)
+    q8_d, sc_d = G.run_quantize(di.q)
+    s_ref = orc.q_scale(wl.q)
+    q8_ref = orc.q_quantize(wl.q, s_ref)
+    ref, ref_lse, ref_err = _oracle_attn(orc, wl, pool, q8_ref, s_ref)
+    out, lse, err = G.run_attn(di, G.dev(pool), phase=1, q=q8_d, q_scale=sc_d)
+    assert err == ref_err == 0
+    G.assert_attn_close(out, ref, where="persistent prefill, two splits")
+    G.assert_lse_close(lse, ref_lse)
+    for t in range(T):
+        if widths[t % len(widths)] == 0:
+            assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
+
+
 def test_q8_prefill_persistent_bad_sequence():
     """Persistent FP8-query prefill units whose token has a sequence id
     outside [0, num_seqs) (a workgroup's first and later units) read
