@@ -548,6 +548,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         constexpr int kPer = kMaxSplit / kThreads;
         constexpr int kPtPer = L::kPtPer;
         constexpr int kPtCap = kPtPer * kThreads;
+        // lane l of wave w resolves entry i of the rows it copies in every
+        // tile: row kRowsPerWave w + (l mod kRowsPerWave) of tile
+        // l / kRowsPerWave + (64 / kRowsPerWave) i, so that its first tiles'
+        // copies read only its own slot stores and go out before the barrier
+        constexpr int kTilesPerI = 64 / kRowsPerWave;
+        static_assert(kPer * kTilesPerI * kTile == kMaxSplit, "every entry once");
+        auto entry_of = [&](int i) {
+            return (lane / kRowsPerWave + kTilesPerI * i) * kTile + kRowsPerWave * w + lane % kRowsPerWave;
+        };
         const int32_t *tk = a.topk + (int64_t)t * a.K + begin;
         const int32_t *row = a.page_table + (int64_t)(seq_ok ? seq : 0) * a.max_pages;
         int32_t *pt_lds = reinterpret_cast<int32_t *>(lds + L::kOffSp);
@@ -559,7 +568,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             for (int k = 0; k < kPtPer; k++) pw[k] = row[min(tid + k * kThreads, a.max_pages - 1)];
 #pragma unroll
             for (int i = 0; i < kPer; i++) {
-                const int j = tid + i * kThreads;
+                const int j = entry_of(i);
                 const int32_t xv = tk[min(j, n_ent - 1)];
                 v[i] = j < n_ent ? xv : -1;
             }
@@ -573,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         } else {
 #pragma unroll
             for (int i = 0; i < kPer; i++) {
-                const int j = tid + i * kThreads;
+                const int j = entry_of(i);
                 const int32_t xv = tk[min(j, n_ent - 1)];
                 v[i] = j < n_ent ? xv : -1;
             }
@@ -586,17 +595,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 for (int i = 0; i < kPer; i++) phys[i] = 0;
             }
         }
-        // last valid entry of each wave (ballot of the resolved slots; j
-        // grows with the lane): the tiles after the split's last valid entry
-        // hold only masked entries, which contribute nothing, and are skipped
+        // the highest tile of each wave holding a valid entry (ballot of the
+        // resolved slots; the tile grows with the lane): the tiles after the
+        // split's last valid entry hold only masked entries, which
+        // contribute nothing, and are skipped
         const TokenIndexRule rule(seq_ok, seq_len, a.page_table != nullptr, a.page_shift, a.max_pages,
                                   a.num_slots);
         int n_err = 0, last = -1;
 #pragma unroll
         for (int i = 0; i < kPer; i++) {
-            const int j = tid + i * kThreads;
-            // (a wave past the split's end holds padding only)
-            if (w * 64 + i * kThreads >= n_ent) continue;
+            const int j = entry_of(i);
+            // (tiles past the split's end hold padding only)
+            if (kTilesPerI * i * kTile >= n_ent) continue;
             bool err;
             const int32_t s = rule(v[i], phys[i], err);
             n_err += __builtin_popcountll(__builtin_amdgcn_ballot_w64(err));   // the wave's
@@ -604,15 +614,40 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                 slots[j] = s >= 0 ? reinterpret_cast<uint64_t>(a.pool + (int64_t)s * row_bytes<LAYOUT>())
                                   : reinterpret_cast<uint64_t>(kZeroRow + (j & (kTile - 1)) * row_bytes<LAYOUT>()) | kMaskBits;
             const uint64_t vb = __builtin_amdgcn_ballot_w64(j < n_ent && s >= 0);
-            if (vb) last = max(last, w * 64 + 63 - (int)__builtin_clzll(vb) + i * kThreads);
+            if (vb) last = max(last, (kTilesPerI * i + (63 - (int)__builtin_clzll(vb)) / kRowsPerWave) * kTile);
         }
         if (lane == 0) reinterpret_cast<int *>(rl_lds)[w] = last;
         if (a.err_count && hb == 0 && lane == 0 && n_err) atomicAdd(a.err_count, n_err);
     }
-    // slots visible; also drains the query and index loads, so that inside
-    // the loop the only outstanding vector-memory operations are tile DMAs
-    __syncthreads();
     const uint32_t lds0 = lds_addr(lds);
+    // Every load issued so far (the index loads, already used, and the
+    // query's register loads) has landed after the wait below, and the
+    // compiler knows it: it then puts no wait of its own behind the copies,
+    // which it does not see.  Then the query copy (kStageQ:
+    // chunk i of the block's kHB rows to LDS position i, holding the row's
+    // chunk (i % kQChunks) unswizzled) and this wave's rows of the first
+    // kFill0 tiles, before the barrier: they read only this wave's slot
+    // stores (the tiles past the last valid entry read masked rows).
+    wait_vm_lgkm0<0>();
+    if constexpr (kStageQ) {
+        const uint32_t qbase = lds_addr(qst);
+#pragma unroll
+        for (int i0 = 0; i0 < kHB * kQChunks; i0 += kThreads) {
+            if (i0 + w * 64 < kHB * kQChunks) {
+                const int i = i0 + w * 64 + lane;
+                const int hl = i / kQChunks, kp = i % kQChunks;
+                dma16(q_global(hl, (kp < 64 ? kp ^ (hl & 7) : kp) << 4), qbase + (i0 + w * 64) * 16);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kFill0; i++)
+        if (i * kTile < n_ent)
+            issue_tile<LAYOUT>(lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
+                                   i, w, lane);
+    // slots and last entries visible (the copies stay in flight)
+    wait_lgkm0();
+    barrier_raw();
     // tiles up to the one holding the last valid entry (at least one: an
     // all-masked split still runs one tile and leaves l = 0)
     int n_tiles;
@@ -627,28 +662,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         n_tiles = __builtin_amdgcn_readfirstlane(max(1, (last + kTile) / kTile));
     }
 
-    // ---- the query copy (kStageQ): chunk i of the block's kHB rows goes to
-    // LDS position i, holding the row's chunk (i % kQChunks) unswizzled
-    if constexpr (kStageQ) {
-        const uint32_t qbase = lds_addr(qst);
-#pragma unroll
-        for (int i0 = 0; i0 < kHB * kQChunks; i0 += kThreads) {
-            if (i0 + w * 64 < kHB * kQChunks) {
-                const int i = i0 + w * 64 + lane;
-                const int hl = i / kQChunks, kp = i % kQChunks;
-                dma16(q_global(hl, (kp < 64 ? kp ^ (hl & 7) : kp) << 4), qbase + (i0 + w * 64) * 16);
-            }
-        }
-    }
-    // ---- fill the pipeline: the first kFill0 tiles now, the other buffers
-    // once tile 0 has landed (requested all at once, every workgroup's first
-    // tile would come back only with the rest of the burst); the buffer
-    // holding the query copy once every wave has its query
-#pragma unroll
-    for (int i = 0; i < kFill0; i++)
-        if (i < n_tiles)
-            issue_tile<LAYOUT>(lds0, read_slots<LAYOUT>(slots, i * kTile, w, lane), i,
-                                   i, w, lane);
+    // ---- fill the pipeline: the first kFill0 tiles went out before the
+    // barrier, the other buffers once tile 0 has landed (requested all at
+    // once, every workgroup's first tile would come back only with the rest
+    // of the burst); the buffer holding the query copy once every wave has
+    // its query
     auto fill_rest = [&](auto last) {
         constexpr bool LAST = decltype(last)::value;
 #pragma unroll
