@@ -13,7 +13,11 @@
 namespace dsa {
 
 constexpr int kQThreads = 256;
-constexpr int kQMaxBlocks = 1024;
+// 8 blocks of 4 waves per compute unit: for a 128 MiB query, 2048 blocks of
+// 2 loads in flight per thread measured 59 us per cast against 66 us for 1024
+// blocks of 4 (4096 blocks: 62; 8192: 80, where the encode's reduction of
+// the partial maxima grows with the block count)
+constexpr int kQMaxBlocks = 2048;
 
 int quantize_q_blocks(int64_t n_elems) {
     int64_t vecs = n_elems / 8;
@@ -39,7 +43,7 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 // Each thread keeps kQUnroll 16-byte loads in flight per pass (grid-stride
 // over 8-element vectors), so the stream is bandwidth- rather than
 // latency-bound.
-constexpr int kQUnroll = 4;
+constexpr int kQUnroll = 2;
 
 __device__ __forceinline__ float amax8(u32x4 raw) {
     float m = 0.0f;
