@@ -1939,7 +1939,8 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
         // differs from the reference, O rescaled when the reference moves), the
         // denominator from the operand (wave 4), then the product over the
         // wave's dims
-        auto pv = [&](int j) {
+        // (next >= 0: then the transpose reads of tile next)
+        auto pv = [&](int j, int next) {
             const int ppar = j & 1;
             const float *mq_lds = reinterpret_cast<const float *>(lds + L::kOffMq + ppar * L::kMqBytes);
             const uint8_t *p_lds = lds + L::kOffP + ppar * L::kPBytes;
@@ -2003,22 +2004,21 @@ __global__ __launch_bounds__(W8::kThreads) void attn_w8_kernel(AttnArgs a) {
                     acc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av1, bp[nt][1], acc[dt][nt], 0, 0, 0);
                 }
             }
+            if (next >= 0) read_tv(next);
         };
 
         barrier_raw();                           // tile 0 and the query copy landed
         read_tv(0);
         wait_lgkm0();
         barrier_raw();                           // (the scoring waves hold the query)
+        // step k: the product of tile k - 1, then tile k's transpose reads
         for (int k = 0; k < n_tiles; k++) {
-            if (k > 0) {
-                pv(k - 1);
-                read_tv(k);
-            }
+            if (k > 0) pv(k - 1, k);
             if (has_next && k == n_tiles - 1) fetch_next(nu, w - 4, kHalf, nwords);
             wait_lgkm0();
             barrier_raw();
         }
-        pv(n_tiles - 1);
+        pv(n_tiles - 1, -1);
         if (has_next) resolve_next(nu, w - 4, kHalf, nwords);
 
         // epilogue: wave 4's denominators through LDS, then O / l
