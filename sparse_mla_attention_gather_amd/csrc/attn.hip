@@ -1411,9 +1411,11 @@ struct W8 {
     static constexpr int kPBytes = kHB * kTile * 2;
     static constexpr int kOffMq = kOffP + 2 * kPBytes;         // quarter maxima [32][4], two
     static constexpr int kMqBytes = kHB * 16;
-    static constexpr int kOffRedL = kOffMq + 2 * kMqBytes;     // last entries, then denominators
+    static constexpr int kOffRedL = kOffMq + 2 * kMqBytes;     // the denominators [32]
     static constexpr int kOffFlags = kOffRedL + kHB * 16;      // [32][4] bytes, two
-    static constexpr int kOffLast = kOffFlags + 2 * kHB * 4;   // a unit's last valid entries [8]
+    // per wave, the first entry of the unit's last tile holding a valid
+    // entry of that wave (-1: none) [8]
+    static constexpr int kOffLast = kOffFlags + 2 * kHB * 4;
     // persistent workgroups: the next unit's page-table row (when it fits),
     // its sequence length (64 copies) and its sequence
     static constexpr int kOffPtN = kOffLast + 8 * 4;
